@@ -1,0 +1,154 @@
+"""Block-scaled (NVFP4 / MXFP4 / MXFP8) quantize + GEMM on MI355X.
+
+Thin Python binding over the C ABI of libbsq.so (include/bsq.h): argument
+marshalling only.  PyTorch supplies device memory and the current stream;
+every step of the computation runs in the HIP kernels of libbsq.so.  If the
+library has not been built (python -m fp8_quantized_gemm_amd._build), every
+entry point raises; there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsq.so")
+
+BSQ_OK, BSQ_EINVAL, BSQ_EUNSUPPORTED, BSQ_EHIP = 0, 1, 2, 3
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "mxfp8": 2}
+ROUNDING = {"rne": 0, "sr": 1}
+ABI_SYMBOLS = ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "bs_gemm",
+               "bsq_status_string")
+
+
+class BsqError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libbsq.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m fp8_quantized_gemm_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, U64, U32, U16 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint16)
+        L.nvfp4_quantize.argtypes = [P, I64, I64, I, I, U64, U32, I, U16, P, P, P, P, P]
+        L.mx_quantize.argtypes = [P, I64, I64, I, I, U64, U32, P, P, P]
+        L.quantize_transpose.argtypes = [P, I64, I64, I, I, I, U64, U32, I, U16,
+                                         P, P, P, P, P, P, P]
+        L.bs_gemm.argtypes = [I, I64, I64, I64, P, P, P, P, P, P, P, I64, P]
+        for fn in ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "bs_gemm"):
+            getattr(L, fn).restype = I
+        L.bsq_status_string.argtypes = [I]
+        L.bsq_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().bsq_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != BSQ_OK:
+        raise BsqError(fn, status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_input(x):
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2):
+        raise ValueError("x must be a 2-D bfloat16 CUDA tensor")
+    return x.contiguous()
+
+
+def _u8(shape, device):
+    return torch.empty(shape, dtype=torch.uint8, device=device)
+
+
+def nvfp4_quantize(x, block_rows=1, rnd="rne", seed=0, offset=0, rht=False, rht_signs=0,
+                   amax=None):
+    """Rowwise NVFP4 of x [R, C] -> (codes uint8 [R, C/2], scales uint8 [R, C/16], amax f32 [1])."""
+    x = _check_input(x)
+    R, C = x.shape
+    codes = _u8((R, C // 2), x.device)
+    scales = _u8((R, max(C // 16, 0)), x.device)
+    amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    st = lib().nvfp4_quantize(_ptr(x), R, C, int(block_rows), ROUNDING[rnd], int(seed), int(offset),
+                              1 if rht else 0, int(rht_signs) & 0xFFFF, _ptr(amax),
+                              _ptr(codes), _ptr(scales), _ptr(amax_out), _stream(x.device))
+    _check("nvfp4_quantize", st)
+    return codes, scales, amax_out
+
+
+def mx_quantize(x, fmt="mxfp4", rnd="rne", seed=0, offset=0):
+    """Rowwise MXFP4 / MXFP8 of x [R, C] -> (codes, scales E8M0 [R, C/32])."""
+    x = _check_input(x)
+    R, C = x.shape
+    codes = _u8((R, C // 2 if fmt == "mxfp4" else C), x.device)
+    scales = _u8((R, C // 32), x.device)
+    st = lib().mx_quantize(_ptr(x), R, C, FORMATS[fmt], ROUNDING[rnd], int(seed), int(offset),
+                           _ptr(codes), _ptr(scales), _stream(x.device))
+    _check("mx_quantize", st)
+    return codes, scales
+
+
+def quantize_transpose(x, fmt="nvfp4", block_rows=1, rnd="rne", seed=0, offset=0,
+                       rht_col=False, rht_signs=0, row=True, col=True):
+    """Row (quantize(x)) and column (quantize(x^T)) outputs from one read of x [R, C].
+
+    Returns a dict with row_codes, row_scales, row_amax, col_codes, col_scales,
+    col_amax (entries of a skipped orientation, and amax for MX, are None)."""
+    x = _check_input(x)
+    R, C = x.shape
+    blk = 16 if fmt == "nvfp4" else 32
+    w = 1 if fmt == "mxfp8" else 2
+    out = dict(row_codes=None, row_scales=None, row_amax=None,
+               col_codes=None, col_scales=None, col_amax=None)
+    if row:
+        out["row_codes"] = _u8((R, C // w), x.device)
+        out["row_scales"] = _u8((R, C // blk), x.device)
+        if fmt == "nvfp4":
+            out["row_amax"] = torch.empty(1, dtype=torch.float32, device=x.device)
+    if col:
+        out["col_codes"] = _u8((C, R // w), x.device)
+        out["col_scales"] = _u8((C, R // blk), x.device)
+        if fmt == "nvfp4":
+            out["col_amax"] = torch.empty(1, dtype=torch.float32, device=x.device)
+    st = lib().quantize_transpose(
+        _ptr(x), R, C, FORMATS[fmt], int(block_rows), ROUNDING[rnd], int(seed), int(offset),
+        1 if rht_col else 0, int(rht_signs) & 0xFFFF,
+        _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_amax"]),
+        _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_amax"]), _stream(x.device))
+    _check("quantize_transpose", st)
+    return out
+
+
+def bs_gemm(fmt, a_codes, a_scales, b_codes, b_scales, a_amax=None, b_amax=None, K=None, out=None):
+    """C [M, N] bf16 = alpha * deq(A) . deq(B)^T with A, B K-major block-scaled operands."""
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    if K is None:
+        K = a_codes.shape[1] * (1 if fmt == "mxfp8" else 2)
+    dev = a_codes.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ldc = out.stride(0) if out.dim() == 2 else N
+    st = lib().bs_gemm(FORMATS[fmt], M, N, int(K), _ptr(a_codes), _ptr(a_scales), _ptr(a_amax),
+                       _ptr(b_codes), _ptr(b_scales), _ptr(b_amax), _ptr(out), ldc, _stream(dev))
+    _check("bs_gemm", st)
+    return out

@@ -1,0 +1,162 @@
+// C-ABI entry points of libbsq: argument validation and kernel dispatch.
+// The contract of every function is documented in include/bsq.h.
+#include "bsq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "bsq_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned16_or_null(const void* p) { return p == nullptr || aligned16(p); }
+
+// Device pointers handed to us must at least be 4-byte aligned for scalars.
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bsq_status hip_status(hipError_t e) { return e == hipSuccess ? BSQ_OK : BSQ_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsq_status_string(bsq_status status) {
+  switch (status) {
+    case BSQ_OK: return "BSQ_OK";
+    case BSQ_EINVAL: return "BSQ_EINVAL: invalid argument (null pointer, size or alignment)";
+    case BSQ_EUNSUPPORTED: return "BSQ_EUNSUPPORTED: combination not defined by the recipe";
+    case BSQ_EHIP: return "BSQ_EHIP: HIP launch error";
+    default: return "BSQ_UNKNOWN";
+  }
+}
+
+bsq_status nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int block_rows,
+                          bsq_rounding rnd, uint64_t seed, uint32_t offset, int rht,
+                          uint16_t rht_signs, const float* amax_in, uint8_t* codes,
+                          uint8_t* scales, float* amax_out, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return BSQ_EINVAL;
+  if (block_rows != 1 && block_rows != 16) return BSQ_EINVAL;
+  if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
+  if (block_rows == 16 && rows % 16 != 0) return BSQ_EINVAL;
+  if (amax_in == nullptr && amax_out == nullptr) return BSQ_EINVAL;
+  if (!aligned4(amax_in) || !aligned4(amax_out)) return BSQ_EINVAL;
+  if (block_rows == 16 && (rnd == BSQ_SR || rht)) return BSQ_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n = rows * cols;
+  if (n == 0) {
+    if (amax_out) return hip_status(bsq::launch_zero_amax(amax_out, nullptr, s));
+    return BSQ_OK;
+  }
+  if (!x || !codes || !scales) return BSQ_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return BSQ_EINVAL;
+
+  const float* amax = amax_in;
+  hipError_t e;
+  if (amax_in == nullptr) {
+    e = bsq::launch_zero_amax(amax_out, nullptr, s);
+    if (e != hipSuccess) return BSQ_EHIP;
+    e = bsq::launch_amax_flat(x, n / 8, rht != 0, rht_signs, amax_out, nullptr, s);
+    if (e != hipSuccess) return BSQ_EHIP;
+    amax = amax_out;
+  } else if (amax_out != nullptr && amax_out != amax_in) {
+    e = bsq::launch_copy_amax(amax_in, amax_out, s);
+    if (e != hipSuccess) return BSQ_EHIP;
+  }
+  if (block_rows == 1)
+    e = bsq::launch_quant_flat(bsq::kNVFP4, rnd == BSQ_SR, rht != 0, x, n / 8, amax, rht_signs,
+                               seed, offset, codes, scales, s);
+  else
+    e = bsq::launch_quant_tile(bsq::kNVFP4, false, false, true, x, rows, cols, true, false, amax,
+                               amax, 0, seed, offset, codes, scales, nullptr, nullptr, s);
+  return hip_status(e);
+}
+
+bsq_status mx_quantize(const void* x, int64_t rows, int64_t cols, bsq_format fmt,
+                       bsq_rounding rnd, uint64_t seed, uint32_t offset, uint8_t* codes,
+                       uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return BSQ_EINVAL;
+  if (fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8) return fmt == BSQ_NVFP4 ? BSQ_EUNSUPPORTED : BSQ_EINVAL;
+  if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
+  if (fmt == BSQ_MXFP8 && rnd == BSQ_SR) return BSQ_EUNSUPPORTED;
+  const int64_t n = rows * cols;
+  if (n == 0) return BSQ_OK;
+  if (!x || !codes || !scales) return BSQ_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return BSQ_EINVAL;
+  return hip_status(bsq::launch_quant_flat(fmt == BSQ_MXFP4 ? bsq::kMXFP4 : bsq::kMXFP8,
+                                           rnd == BSQ_SR, false, x, n / 8, nullptr, 0, seed,
+                                           offset, codes, scales,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_format fmt,
+                              int block_rows, bsq_rounding rnd, uint64_t seed, uint32_t offset,
+                              int rht_col, uint16_t rht_signs, uint8_t* codes_row,
+                              uint8_t* scales_row, float* amax_row, uint8_t* codes_col,
+                              uint8_t* scales_col, float* amax_col, void* stream) {
+  if (fmt != BSQ_NVFP4 && fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8) return BSQ_EINVAL;
+  const bool nv = fmt == BSQ_NVFP4;
+  const int blk = nv ? 16 : 32;
+  if (rows < 0 || cols < 0 || rows % blk != 0 || cols % blk != 0) return BSQ_EINVAL;
+  if (block_rows != 1 && block_rows != 16) return BSQ_EINVAL;
+  if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
+  const bool do_row = codes_row || scales_row || (nv && amax_row);
+  const bool do_col = codes_col || scales_col || (nv && amax_col);
+  if (!do_row && !do_col) return BSQ_EINVAL;
+  if (do_row && (!codes_row || !scales_row || (nv && !amax_row))) return BSQ_EINVAL;
+  if (do_col && (!codes_col || !scales_col || (nv && !amax_col))) return BSQ_EINVAL;
+  if (!aligned16_or_null(codes_row) || !aligned16_or_null(scales_row) ||
+      !aligned16_or_null(codes_col) || !aligned16_or_null(scales_col))
+    return BSQ_EINVAL;
+  if (nv && (!aligned4(amax_row) || !aligned4(amax_col))) return BSQ_EINVAL;
+  if (!nv && (block_rows == 16 || rht_col)) return BSQ_EUNSUPPORTED;
+  if (fmt == BSQ_MXFP8 && rnd == BSQ_SR) return BSQ_EUNSUPPORTED;
+  if (block_rows == 16 && (rnd == BSQ_SR || rht_col)) return BSQ_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ar = do_row ? amax_row : nullptr;
+  float* ac = do_col ? amax_col : nullptr;
+  if (rows * cols == 0) {
+    if (nv) return hip_status(bsq::launch_zero_amax(ar, ac, s));
+    return BSQ_OK;
+  }
+  if (!x || !aligned16(x)) return BSQ_EINVAL;
+
+  hipError_t e;
+  if (nv) {
+    e = bsq::launch_zero_amax(ar, ac, s);
+    if (e != hipSuccess) return BSQ_EHIP;
+    if (rht_col && do_col)
+      e = bsq::launch_amax_tile_rht(x, rows, cols, rht_signs, ar, ac, s);
+    else
+      e = bsq::launch_amax_flat(x, rows * cols / 8, false, 0, ar ? ar : ac, ar ? ac : nullptr, s);
+    if (e != hipSuccess) return BSQ_EHIP;
+  }
+  const bsq::Fmt f = nv ? bsq::kNVFP4 : (fmt == BSQ_MXFP4 ? bsq::kMXFP4 : bsq::kMXFP8);
+  e = bsq::launch_quant_tile(f, rnd == BSQ_SR, rht_col != 0 && do_col, block_rows == 16, x, rows,
+                             cols, do_row, do_col, ar, ac, rht_signs, seed, offset, codes_row,
+                             scales_row, codes_col, scales_col, s);
+  return hip_status(e);
+}
+
+bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                   const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
+                   const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,
+                   void* stream) {
+  if (fmt != BSQ_NVFP4 && fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8) return BSQ_EINVAL;
+  if (M < 0 || N < 0 || K < 0) return BSQ_EINVAL;
+  if (K % (fmt == BSQ_NVFP4 ? 16 : 32) != 0) return BSQ_EINVAL;
+  if (ldc < N || ldc < 0) return BSQ_EINVAL;
+  if (M > (int64_t)256 * 0x7FFFFF || N > (int64_t)256 * 0x7FFFFF) return BSQ_EINVAL;
+  if (M == 0 || N == 0) return BSQ_OK;
+  if (!c || ((reinterpret_cast<uintptr_t>(c) & 1u) != 0)) return BSQ_EINVAL;
+  if (K > 0) {
+    if (!a_codes || !a_scales || !b_codes || !b_scales) return BSQ_EINVAL;
+    if (fmt == BSQ_NVFP4 && (!a_amax || !b_amax)) return BSQ_EINVAL;
+  } else if (fmt == BSQ_NVFP4 && (!a_amax || !b_amax)) {
+    return BSQ_EINVAL;
+  }
+  const bsq::Fmt f = fmt == BSQ_NVFP4 ? bsq::kNVFP4 : (fmt == BSQ_MXFP4 ? bsq::kMXFP4 : bsq::kMXFP8);
+  return hip_status(bsq::launch_gemm(f, M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales,
+                                     b_amax, c, ldc, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+// Device-side codecs for the block quantizers (gfx950).
+//
+// E2M1 / E4M3 / E8M0 encoders, the NVFP4 block-scale step, the 16-point
+// Hadamard butterfly and Philox4x32-10.  Every function reproduces the
+// numerical contract stated in include/bsq.h bit for bit: IEEE float32 RNE
+// operations, denormals kept (the default gfx950 float mode), and this file
+// is compiled with -ffp-contract=off so no multiply-add is fused.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsq {
+
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+
+// BF16 halves of a packed dword -> float32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- E2M1
+// Magnitude code (0..7) of a = |v| by round-to-nearest, ties to the even code,
+// saturating at 6 (OCP MX E2M1 element).
+//  * a < 1: the grid is {0, 0.5, 1}; the code is (a > 0.25) + (a >= 0.75).
+//  * a >= 1: E2M1 is a float with one significand bit, so rounding the FP32
+//    significand to one bit (add 0x1FFFFF plus the kept bit, then drop 22
+//    bits) gives ((exp - 127) * 2 + mantissa bit), offset so 1.0 -> code 2.
+// For finite a >= 0 float ordering equals unsigned ordering of the bits.
+__device__ __forceinline__ uint32_t e2m1_rne_mag(float a) {
+  const uint32_t b = f2u(a);
+  const uint32_t lo = (b > 0x3E800000u ? 1u : 0u) + (b >= 0x3F400000u ? 1u : 0u);
+  const uint32_t r = (b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22;
+  const uint32_t hi = min(r - 252u, 7u);
+  return b < 0x3F800000u ? lo : hi;
+}
+
+// Magnitude code of a = |v| by stochastic rounding with a 16-bit random word:
+// with lo <= a < hi the neighbouring grid magnitudes, round up iff
+// r16 < floor((a - lo) / (hi - lo) * 65536).  The grid spacing is 0.5 on
+// [0, 2), 1 on [2, 4) and 2 on [4, 6), so q = a / spacing is exact, its
+// integer part indexes lo and q - floor(q) is the exact fraction.
+__device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t r16) {
+  if (!(a < 6.0f)) return 7u;
+  const bool r0 = a < 2.0f, r1 = a < 4.0f;
+  const float inv_step = r0 ? 2.0f : (r1 ? 1.0f : 0.5f);
+  const uint32_t base = r0 ? 0u : (r1 ? 2u : 4u);
+  const float q = a * inv_step;
+  const float fl = __builtin_floorf(q);
+  const float frac = q - fl;
+  const uint32_t t = (uint32_t)(frac * 65536.0f);   // truncation == floor here
+  return base + (uint32_t)fl + (r16 < t ? 1u : 0u);
+}
+
+// Signed 4-bit code: magnitude | sign bit of v.
+__device__ __forceinline__ uint32_t e2m1_sign(float v) { return (f2u(v) >> 28) & 8u; }
+
+// ---------------------------------------------------------------- E4M3
+// OCP E4M3FN code (0..0x7E) of a >= 0 by RNE, saturating at 448, subnormals
+// kept.  Normal range: round the FP32 significand to 3 bits (drop 20 bits with
+// the ties-to-even bias) and rebias the exponent (127 - 7) << 3 = 960;
+// a significand carry increments the exponent field by itself.
+__device__ __forceinline__ uint32_t e4m3_rne_mag(float a) {
+  const uint32_t b = f2u(a);
+  if (b > 0x43E00000u) return 0x7Eu;                 // > 448 (and Inf / NaN)
+  if (b < 0x3C800000u)                                // < 2^-6: grid 2^-9
+    return (uint32_t)__builtin_rintf(a * 512.0f);    // 0..8 (8 = min normal)
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  return (r >> 20) - 960u;
+}
+
+// Decode an unsigned E4M3 code (0..0x7E) exactly.
+__device__ __forceinline__ float e4m3_decode_mag(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? u2f(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// ---------------------------------------------------------------- NVFP4 scales
+// Per-tensor encode scale: 2688 / amax (2688 = 448 * 6), 1 for amax == 0,
+// at most FLT_MAX.
+__device__ __forceinline__ float nvfp4_s_enc(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  return fminf(2688.0f / amax, kFltMax);
+}
+
+// Block step: sf = (a_b / 6) * s_enc; S = E4M3(sf); enc = s_enc / S (0 if S == 0).
+struct BlockScale {
+  uint32_t code;
+  float enc;
+};
+__device__ __forceinline__ BlockScale nvfp4_block_scale(float a_b, float s_enc) {
+  const float t = a_b / 6.0f;
+  const float sf = t * s_enc;
+  BlockScale bs;
+  bs.code = e4m3_rne_mag(sf);
+  const float sfq = e4m3_decode_mag(bs.code);
+  bs.enc = sfq == 0.0f ? 0.0f : fminf(s_enc / sfq, kFltMax);
+  return bs;
+}
+
+// ---------------------------------------------------------------- E8M0 (MX)
+// floor(log2 a) for finite a > 0, including FP32 subnormals.
+__device__ __forceinline__ int floor_log2(float a) {
+  const uint32_t b = f2u(a);
+  if (b >= 0x00800000u) return (int)(b >> 23) - 127;
+  return (31 - (int)__builtin_clz(b)) - 149;
+}
+
+// Shared MX exponent of a block with amax a_b: floor(log2 a_b) - emax, -127 for
+// a zero block, clamped to [-127, 127].
+__device__ __forceinline__ int mx_exponent(float a_b, int emax) {
+  if (a_b == 0.0f) return -127;
+  const int e = floor_log2(a_b) - emax;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^-e as an exact float32 (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float exp2_neg(int e) {
+  const int k = 127 - e;                 // biased exponent of 2^-e
+  return k >= 1 ? u2f((uint32_t)k << 23) : u2f(0x00400000u);
+}
+
+// ---------------------------------------------------------------- RHT
+// y <- 0.25 * H16 * D * y on 16 values held in one thread (natural-order
+// Sylvester H16; bit i of signs negates element i first).
+__device__ __forceinline__ void rht16(float (&y)[16], uint32_t signs) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = u2f(f2u(y[i]) ^ (((signs >> i) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = y[i] * 0.25f;
+}
+
+// ---------------------------------------------------------------- cross-lane
+// quad_perm DPP moves: lane ^ 1 and lane ^ 2 within each group of four lanes.
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float dpp_xor1f(float v) { return u2f(dpp_xor1(f2u(v))); }
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11).  Ten rounds; multipliers 0xD2511F53 / 0xCD9E8D57; Weyl key bumps
+// 0x9E3779B9 / 0xBB67AE85.
+struct U4 {
+  uint32_t x, y, z, w;
+};
+__device__ __forceinline__ U4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                       uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c0 = n0;
+    c1 = (uint32_t)p1;
+    c2 = n2;
+    c3 = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// Eight 16-bit random words for elements idx = 8*grp + j, j = 0..7 (word j>>1,
+// low half for even j).
+struct R16x8 {
+  uint32_t w[4];
+  __device__ __forceinline__ uint32_t get(int j) const { return (w[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu; }
+};
+__device__ __forceinline__ R16x8 sr_words(uint64_t grp, uint64_t seed, uint32_t offset, uint32_t stream) {
+  const U4 r = philox10((uint32_t)grp, (uint32_t)(grp >> 32), offset, stream,
+                        (uint32_t)seed, (uint32_t)(seed >> 32));
+  R16x8 o;
+  o.w[0] = r.x;
+  o.w[1] = r.y;
+  o.w[2] = r.z;
+  o.w[3] = r.w;
+  return o;
+}
+
+}  // namespace bsq

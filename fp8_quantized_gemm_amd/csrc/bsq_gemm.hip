@@ -1,0 +1,423 @@
+// Block-scaled GEMM for gfx950: C[M, N] (BF16) = alpha * A[M, K] . B[N, K]^T.
+//
+// NVFP4 pretraining post, data-flow paragraph after Figure 1: the FPROP, DGRAD
+// and WGRAD GEMMs consume NVFP4 operands and emit BF16.  HN page opcode84: MX
+// formats apply the block scale inside the matrix unit.
+//
+// Routes on CDNA4:
+//  * MXFP8 / MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4 takes one E8M0 scale per
+//    lane per 32-element K block, which is exactly the MX block, so codes go
+//    from LDS straight into the MFMA.
+//  * NVFP4: the 16-element E4M3 block scale is not an MFMA scale type.  Each
+//    E2M1 value times an E4M3 scale has at most 6 significant bits and lies in
+//    [2^-10, 2688], so it is exact in BF16: the codes are expanded in
+//    registers to BF16 products and fed to v_mfma_f32_32x32x16_bf16 (FP32
+//    accumulate).  The per-tensor scales multiply the FP32 result once.
+//
+// Tiling: 256x256 output tile per 512-thread block (8 waves as 2 x 4, each
+// wave 128 (M) x 64 (N) = 4 x 2 MFMA tiles of 32x32), K stage of 128
+// (NVFP4, MXFP8) or 256 (MXFP4) elements, LDS double buffer, one barrier per
+// stage.  Each wave computes D = B_tile . A_tile^T so that every lane holds 4
+// consecutive output columns of a row (8-byte BF16 stores).
+//
+// K order inside a stage: an MFMA only needs A and B to agree on which K index
+// sits in which slot, so lane half h takes one contiguous run of the stage
+// (NVFP4: elements [64h, 64h+64), 8 per step over 8 steps; MX: one 32-element
+// block per step) and reads it from LDS with 16-byte loads.
+#include "bsq_internal.hpp"
+
+namespace bsq {
+
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBM = 256, kBN = 256, kThreads = 512;
+
+template <int FMT>
+struct Cfg {
+  static constexpr int BK = FMT == kMXFP4 ? 256 : 128;                 // K elements per stage
+  static constexpr int RB = FMT == kMXFP8 ? BK : BK / 2;               // code bytes per row per stage
+  static constexpr int SB = FMT == kNVFP4 ? BK / 16 : BK / 32;         // scale bytes per row per stage
+  static constexpr int LDR = RB + 16;                                  // padded LDS row stride
+  static constexpr int CODE_BYTES = kBM * LDR;                         // per operand per stage
+  static constexpr int SCALE_BYTES = kBM * SB;
+  static constexpr int STAGE_BYTES = 2 * CODE_BYTES + 2 * SCALE_BYTES;
+  static constexpr int CHUNKS = kBM * RB / 16;                         // 16B code chunks per operand
+  static constexpr int CPT = CHUNKS / kThreads;                        // per thread
+  static constexpr int STEPS = FMT == kNVFP4 ? BK / 16 : BK / 64;      // MFMA K steps per stage
+};
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;     // NaN stays NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E4M3 byte `sel` of w -> float (exact; OCP E4M3FN on gfx950).
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
+// 8 E2M1 codes (one dword, element 2b in the low nibble of byte b) times a
+// float scale -> 8 BF16 values, exact.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Scaled MFMA with the scale byte chosen by the K step (the byte select must be
+// an immediate).
+template <int FMTC>
+__device__ __forceinline__ floatx16 mfma_mx(int step, const intx8& a, const intx8& b,
+                                            const floatx16& c, uint32_t sa, uint32_t sb) {
+  switch (step) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMTC, FMTC, 0, (int)sa, 0, (int)sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMTC, FMTC, 1, (int)sa, 1, (int)sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMTC, FMTC, 2, (int)sa, 2, (int)sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMTC, FMTC, 3, (int)sa, 3, (int)sb);
+  }
+}
+
+__device__ __forceinline__ float nvfp4_s_dec(float amax) {
+  const float s_enc = amax == 0.0f ? 1.0f : fminf(2688.0f / amax, 3.40282346638528859812e+38f);
+  return 1.0f / s_enc;
+}
+
+// Global -> register staging of one stage of one operand (codes + scales).
+template <int FMT>
+struct Stage {
+  uint4 code[Cfg<FMT>::CPT];
+  uint32_t scale[2];          // this thread's share of the scale rows (8 bytes max)
+};
+
+// Load stage kt of an operand with rows [row0, row0+256) of a [rows, K] matrix.
+// Fast path: whole 16-byte chunks and whole scale words (K % BK == 0 and
+// aligned pointers).  Generic path: byte loads with K bounds (zeros past K).
+template <int FMT, bool FAST>
+__device__ __forceinline__ void load_stage(Stage<FMT>& st, const uint8_t* __restrict__ codes,
+                                           const uint8_t* __restrict__ scales, int64_t rows,
+                                           int64_t row0, int64_t kt, int64_t code_ld,
+                                           int64_t scale_ld) {
+  using C = Cfg<FMT>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int ch = t + i * kThreads;
+    const int r = ch / (C::RB / 16), c16 = ch % (C::RB / 16);
+    int64_t gr = row0 + r;
+    gr = gr < rows ? gr : rows - 1;
+    const int64_t kb = kt * C::RB + c16 * 16;            // byte offset along K
+    if constexpr (FAST) {
+      st.code[i] = *reinterpret_cast<const uint4*>(codes + gr * code_ld + kb);
+    } else {
+      uint8_t b[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) b[j] = (kb + j < code_ld) ? codes[gr * code_ld + kb + j] : 0;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = b[4 * j] | (b[4 * j + 1] << 8) | (b[4 * j + 2] << 16) | ((uint32_t)b[4 * j + 3] << 24);
+      st.code[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  // scales: thread t < 256 loads row t's SB bytes (SB is 4 or 8)
+  st.scale[0] = st.scale[1] = 0;
+  if (t < kBM) {
+    int64_t gr = row0 + t;
+    gr = gr < rows ? gr : rows - 1;
+    const int64_t sb = kt * C::SB;
+    if constexpr (FAST) {
+      if (C::SB == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(scales + gr * scale_ld + sb);
+        st.scale[0] = v.x;
+        st.scale[1] = v.y;
+      } else {
+        st.scale[0] = *reinterpret_cast<const uint32_t*>(scales + gr * scale_ld + sb);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::SB; ++j) {
+        const uint32_t b = (sb + j < scale_ld) ? scales[gr * scale_ld + sb + j] : 0;
+        st.scale[j >> 2] |= b << (8 * (j & 3));
+      }
+    }
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_stage(const Stage<FMT>& st, uint8_t* lds_codes,
+                                            uint8_t* lds_scales) {
+  using C = Cfg<FMT>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int ch = t + i * kThreads;
+    const int r = ch / (C::RB / 16), c16 = ch % (C::RB / 16);
+    *reinterpret_cast<uint4*>(lds_codes + r * C::LDR + c16 * 16) = st.code[i];
+  }
+  if (t < kBM) {
+    if (C::SB == 8)
+      *reinterpret_cast<uint2*>(lds_scales + t * 8) = make_uint2(st.scale[0], st.scale[1]);
+    else
+      *reinterpret_cast<uint32_t*>(lds_scales + t * 4) = st.scale[0];
+  }
+}
+
+template <int FMT, bool FAST>
+__global__ __launch_bounds__(kThreads) void k_gemm(
+    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes,
+    const uint8_t* __restrict__ a_scales, const float* __restrict__ a_amax,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
+    const float* __restrict__ b_amax, uint16_t* __restrict__ c, int64_t ldc, int tiles_m,
+    int tiles_n, int vec_store) {
+  using C = Cfg<FMT>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  // grouped tile order: 8 M-tiles share each sweep over N for L2 reuse
+  const int pid = blockIdx.x;
+  constexpr int GROUP = 8;
+  const int group_size = GROUP * tiles_n;
+  const int gid = pid / group_size;
+  const int first_m = gid * GROUP;
+  const int gm = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (pid % group_size) % gm;
+  const int tn = (pid % group_size) / gm;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 2, wn = wave & 3;            // 2 x 4 waves
+  const int h = lane >> 5, l32 = lane & 31;
+
+  const int64_t code_ld = FMT == kMXFP8 ? K : K / 2;
+  const int64_t scale_ld = FMT == kNVFP4 ? K / 16 : K / 32;
+  const int64_t KT = (K + C::BK - 1) / C::BK;
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  auto lds_a = [&](int buf) { return smem + buf * C::STAGE_BYTES; };
+  auto lds_b = [&](int buf) { return smem + buf * C::STAGE_BYTES + C::CODE_BYTES; };
+  auto lds_sa = [&](int buf) { return smem + buf * C::STAGE_BYTES + 2 * C::CODE_BYTES; };
+  auto lds_sb = [&](int buf) {
+    return smem + buf * C::STAGE_BYTES + 2 * C::CODE_BYTES + C::SCALE_BYTES;
+  };
+
+  Stage<FMT> sa, sb;
+  if (KT > 0) {
+    load_stage<FMT, FAST>(sa, a_codes, a_scales, M, m0, 0, code_ld, scale_ld);
+    load_stage<FMT, FAST>(sb, b_codes, b_scales, N, n0, 0, code_ld, scale_ld);
+    store_stage<FMT>(sa, lds_a(0), lds_sa(0));
+    store_stage<FMT>(sb, lds_b(0), lds_sb(0));
+  }
+  __syncthreads();
+
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    const int buf = (int)(kt & 1);
+    const bool more = kt + 1 < KT;
+    if (more) {
+      load_stage<FMT, FAST>(sa, a_codes, a_scales, M, m0, kt + 1, code_ld, scale_ld);
+      load_stage<FMT, FAST>(sb, b_codes, b_scales, N, n0, kt + 1, code_ld, scale_ld);
+    }
+    const uint8_t* La = lds_a(buf);
+    const uint8_t* Lb = lds_b(buf);
+    const uint8_t* LSa = lds_sa(buf);
+    const uint8_t* LSb = lds_sb(buf);
+
+    if constexpr (FMT == kNVFP4) {
+      // lane half h owns stage elements [64h, 64h + 64): 32 code bytes, 4 scale bytes
+      uint32_t sca[4], scb[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        sca[mi] = *reinterpret_cast<const uint32_t*>(LSa + (wm * 128 + mi * 32 + l32) * 8 + 4 * h);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        scb[ni] = *reinterpret_cast<const uint32_t*>(LSb + (wn * 64 + ni * 32 + l32) * 8 + 4 * h);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {          // 16-byte reads: 4 K-steps each
+        uint4 ca[4], cb[2];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          ca[mi] = *reinterpret_cast<const uint4*>(La + (wm * 128 + mi * 32 + l32) * C::LDR +
+                                                   32 * h + 16 * half);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          cb[ni] = *reinterpret_cast<const uint4*>(Lb + (wn * 64 + ni * 32 + l32) * C::LDR +
+                                                   32 * h + 16 * half);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          // K step (4*half + s) covers lane elements 8*(4*half+s) .. +7 -> scale byte 2*half + s/2
+          bf16x8 fa[4], fb[2];
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) {
+            const uint32_t w = s == 0 ? ca[mi].x : s == 1 ? ca[mi].y : s == 2 ? ca[mi].z : ca[mi].w;
+            const float scl = half == 0 ? (s < 2 ? e4m3_to_f32<0>(sca[mi]) : e4m3_to_f32<1>(sca[mi]))
+                                        : (s < 2 ? e4m3_to_f32<2>(sca[mi]) : e4m3_to_f32<3>(sca[mi]));
+            fa[mi] = dequant8(w, scl);
+          }
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) {
+            const uint32_t w = s == 0 ? cb[ni].x : s == 1 ? cb[ni].y : s == 2 ? cb[ni].z : cb[ni].w;
+            const float scl = half == 0 ? (s < 2 ? e4m3_to_f32<0>(scb[ni]) : e4m3_to_f32<1>(scb[ni]))
+                                        : (s < 2 ? e4m3_to_f32<2>(scb[ni]) : e4m3_to_f32<3>(scb[ni]));
+            fb[ni] = dequant8(w, scl);
+          }
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
+        }
+      }
+    } else {
+      // MX: lane half h, step s uses the 32-element block h*STEPS + s of the stage
+      constexpr int EB = FMT == kMXFP8 ? 32 : 16;     // bytes per 32-element block
+      constexpr int FMTC = FMT == kMXFP8 ? 0 : 4;     // cbsz / blgp operand type
+      uint32_t sca[4], scb[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const uint8_t* p = LSa + (wm * 128 + mi * 32 + l32) * C::SB + h * C::STEPS;
+        sca[mi] = C::STEPS == 4 ? *reinterpret_cast<const uint32_t*>(p)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const uint8_t* p = LSb + (wn * 64 + ni * 32 + l32) * C::SB + h * C::STEPS;
+        scb[ni] = C::STEPS == 4 ? *reinterpret_cast<const uint32_t*>(p)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+      }
+#pragma unroll
+      for (int s = 0; s < C::STEPS; ++s) {
+        intx8 fa[4], fb[2];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const uint8_t* p = La + (wm * 128 + mi * 32 + l32) * C::LDR + (h * C::STEPS + s) * EB;
+          const uint4 lo = *reinterpret_cast<const uint4*>(p);
+          uint4 hi = make_uint4(0, 0, 0, 0);
+          if (EB == 32) hi = *reinterpret_cast<const uint4*>(p + 16);
+          fa[mi] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const uint8_t* p = Lb + (wn * 64 + ni * 32 + l32) * C::LDR + (h * C::STEPS + s) * EB;
+          const uint4 lo = *reinterpret_cast<const uint4*>(p);
+          uint4 hi = make_uint4(0, 0, 0, 0);
+          if (EB == 32) hi = *reinterpret_cast<const uint4*>(p + 16);
+          fb[ni] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = mfma_mx<FMTC>(s, fb[ni], fa[mi], acc[mi][ni], scb[ni], sca[mi]);
+        __builtin_amdgcn_sched_barrier(0);      // keep each step's fragments short-lived
+      }
+    }
+
+    if (more) {
+      store_stage<FMT>(sa, lds_a(buf ^ 1), lds_sa(buf ^ 1));
+      store_stage<FMT>(sb, lds_b(buf ^ 1), lds_sb(buf ^ 1));
+    }
+    __syncthreads();
+  }
+
+  // epilogue: alpha * acc -> BF16 (RNE).  Lane holds column m = l32 of D = C^T,
+  // rows n = 8*(r/4) + 4*h + r%4 of each 32x32 tile.
+  float alpha = 1.0f;
+  if (FMT == kNVFP4) alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int64_t m = m0 + wm * 128 + mi * 32 + l32;
+    if (m >= M) continue;
+    uint16_t* crow = c + m * ldc;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * 64 + ni * 32 + 8 * q + 4 * h;
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(acc[mi][ni][4 * q + e] * alpha);
+        if (vec_store && n + 3 < N) {
+          *reinterpret_cast<uint2*>(crow + n) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) crow[n + e] = (uint16_t)b[e];
+        }
+      }
+    }
+  }
+}
+
+template <int FMT>
+hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                         const float* aa, const uint8_t* bc, const uint8_t* bs, const float* ba,
+                         void* c, int64_t ldc, hipStream_t s) {
+  using C = Cfg<FMT>;
+  const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
+  const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const int64_t code_ld = FMT == kMXFP8 ? K : K / 2;
+  const int64_t scale_ld = FMT == kNVFP4 ? K / 16 : K / 32;
+  const bool fast = (K % C::BK == 0) && al16(ac) && al16(bc) && (code_ld % 16 == 0) &&
+                    ((scale_ld * 1) % C::SB == 0) &&
+                    ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(bs)) % C::SB == 0);
+  const bool vec_store = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(c) & 7) == 0);
+  const size_t lds = 2 * (size_t)C::STAGE_BYTES;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<FMT, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<FMT, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return hipErrorInvalidConfiguration;
+    attr_set = true;
+  }
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
+  uint16_t* cp = static_cast<uint16_t*>(c);
+  if (fast)
+    hipLaunchKernelGGL((k_gemm<FMT, true>), grid, block, lds, s, M, N, K, ac, as, aa, bc, bs, ba,
+                       cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
+  else
+    hipLaunchKernelGGL((k_gemm<FMT, false>), grid, block, lds, s, M, N, K, ac, as, aa, bc, bs, ba,
+                       cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                       const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
+                       const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,
+                       hipStream_t s) {
+  switch (fmt) {
+    case kNVFP4:
+      return launch_gemm_t<kNVFP4>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax,
+                                   c, ldc, s);
+    case kMXFP4:
+      return launch_gemm_t<kMXFP4>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax,
+                                   c, ldc, s);
+    default:
+      return launch_gemm_t<kMXFP8>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax,
+                                   c, ldc, s);
+  }
+}
+
+}  // namespace bsq

@@ -1,0 +1,47 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsq {
+
+enum Fmt { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2 };
+
+// Sets *a = 0 and *b = 0 (either may be null).
+hipError_t launch_zero_amax(float* a, float* b, hipStream_t s);
+// *dst = *src.
+hipError_t launch_copy_amax(const float* src, float* dst, hipStream_t s);
+
+// amax over a contiguous BF16 tensor of nchunk 8-element chunks; with rht the
+// amax is over the 16-point RHT of each aligned 16-chunk.  Atomically maxes
+// into a0 and (if non-null) a1, which must have been zeroed.
+hipError_t launch_amax_flat(const void* x, int64_t nchunk, bool rht, uint32_t signs,
+                            float* a0, float* a1, hipStream_t s);
+
+// amax of x (into amax_row, may be null) and of the RHT of x^T along rows
+// (into amax_col) for x [R, C].
+hipError_t launch_amax_tile_rht(const void* x, int64_t R, int64_t C, uint32_t signs,
+                                float* amax_row, float* amax_col, hipStream_t s);
+
+// Rowwise quantization over a contiguous tensor of nchunk 8-element chunks
+// (NVFP4 1x16 or MX 1x32 blocks; rows are implied since cols % block == 0).
+hipError_t launch_quant_flat(Fmt fmt, bool sr, bool rht, const void* x, int64_t nchunk,
+                             const float* amax, uint32_t signs, uint64_t seed, uint32_t offset,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+
+// Row and/or column quantization of x [R, C] from one read.
+hipError_t launch_quant_tile(Fmt fmt, bool sr, bool rht_col, bool two_d, const void* x,
+                             int64_t R, int64_t C, bool do_row, bool do_col,
+                             const float* amax_row, const float* amax_col, uint32_t signs,
+                             uint64_t seed, uint32_t offset, uint8_t* codes_row,
+                             uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                             hipStream_t s);
+
+// C[M, N] = alpha * A . B^T, block-scaled operands, BF16 out.
+hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                       const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
+                       const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,
+                       hipStream_t s);
+
+}  // namespace bsq

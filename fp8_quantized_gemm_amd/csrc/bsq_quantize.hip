@@ -1,0 +1,507 @@
+// Block quantizers for gfx950: amax passes, rowwise (flat) encoder and the
+// row+column (tile) encoder.
+//
+// NVFP4 pretraining post, "NVFP4 pretraining recipe": 1x16 E4M3 block scales
+// under a per-tensor FP32 scale (ingredients 1-2), RHT on WGRAD inputs
+// (ingredient 3), 16x16 weight tiles (ingredient 4), RNE / stochastic rounding
+// (ingredient 5).  HN page opcode84: MXFP4 / MXFP8 with E8M0 scales per 32.
+//
+// Memory layout and work split (all kernels are HBM-bound streams):
+//  * Every lane moves 16-byte chunks of 8 BF16 values and every global access
+//    instruction of a wave covers one contiguous run (1 KiB of input; codes
+//    and scales contiguous across lanes).
+//  * Rowwise: a 1x16 block is a lane pair, a 1x32 MX block a lane quad; the
+//    block amax is combined with quad_perm DPP moves, no LDS.
+//  * Row + column: a lane owns 8 columns x 16 (or 32) rows, so each column
+//    block sits in one lane's registers (the transpose happens in registers)
+//    and each row block is again a lane pair/quad.  A lane walks down several
+//    row blocks so its column outputs fill whole cache lines over time.
+#include "bsq_device.hpp"
+#include "bsq_internal.hpp"
+
+namespace bsq {
+
+namespace {
+
+constexpr int kUnroll = 4;          // chunks per lane per loop trip (flat kernels)
+
+__device__ __forceinline__ uint32_t absbits(float v) { return f2u(v) & 0x7FFFFFFFu; }
+
+// 8 floats from a 16-byte chunk of BF16 values (element e = half e of the chunk).
+__device__ __forceinline__ void unpack8(const uint4& v, float (&y)[8]) {
+  y[0] = bf16_lo(v.x); y[1] = bf16_hi(v.x);
+  y[2] = bf16_lo(v.y); y[3] = bf16_hi(v.y);
+  y[4] = bf16_lo(v.z); y[5] = bf16_hi(v.z);
+  y[6] = bf16_lo(v.w); y[7] = bf16_hi(v.w);
+}
+
+// Element (row i, column j) of a lane's 8-column tile held as rows of uint4.
+__device__ __forceinline__ float tile_elem(const uint4& row, int j) {
+  const uint32_t w = (j >> 1) == 0 ? row.x : (j >> 1) == 1 ? row.y : (j >> 1) == 2 ? row.z : row.w;
+  return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// 16-point RHT of a 16-chunk split over a lane pair: this lane holds elements
+// 8*odd .. 8*odd+7.  Stages h = 1, 2, 4 are in-lane, h = 8 pairs the lanes.
+__device__ __forceinline__ void rht16_pair(float (&y)[8], bool odd, uint32_t signs) {
+  const uint32_t sg = odd ? (signs >> 8) : signs;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = u2f(f2u(y[e]) ^ (((sg >> e) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if ((e & h) == 0) {
+        const float a = y[e], b = y[e + h];
+        y[e] = a + b;
+        y[e + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = dpp_xor1f(y[e]);
+    y[e] = odd ? (p - y[e]) : (y[e] + p);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = y[e] * 0.25f;
+}
+
+// Encode 8 scaled values to 8 E2M1 codes packed low-nibble-first.
+template <bool SR>
+__device__ __forceinline__ uint32_t encode8_fp4(const float (&v)[8], const R16x8& rnd) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float a = __builtin_fabsf(v[e]);
+    const uint32_t m = SR ? e2m1_sr_mag(a, rnd.get(e)) : e2m1_rne_mag(a);
+    out |= (m | e2m1_sign(v[e])) << (4 * e);
+  }
+  return out;
+}
+
+// Encode 8 scaled values to 8 signed E4M3 bytes.
+__device__ __forceinline__ uint2 encode8_fp8(const float (&v)[8]) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t c = e4m3_rne_mag(__builtin_fabsf(v[e])) | ((f2u(v[e]) >> 24) & 0x80u);
+    w[e >> 2] |= c << (8 * (e & 3));
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  return m;
+}
+
+// Block-level max into one or two global accumulators.
+__device__ __forceinline__ void block_max_atomic(uint32_t m, float* a0, float* a1) {
+  __shared__ uint32_t red[16];
+  m = wave_max_u32(m);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int nw = (blockDim.x + 63) >> 6;
+    for (int i = 1; i < nw; ++i) m = max(m, red[i]);
+    if (a0) atomicMax(reinterpret_cast<unsigned int*>(a0), m);
+    if (a1) atomicMax(reinterpret_cast<unsigned int*>(a1), m);
+  }
+}
+
+// ---------------------------------------------------------------- small kernels
+
+__global__ void k_zero_amax(float* a, float* b) {
+  if (threadIdx.x == 0) {
+    if (a) *a = 0.0f;
+    if (b) *b = 0.0f;
+  }
+}
+
+__global__ void k_copy_amax(const float* src, float* dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
+// ---------------------------------------------------------------- amax passes
+
+template <bool RHT>
+__global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, int64_t nchunk,
+                                                   uint32_t signs, float* a0, float* a1) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  uint32_t m = 0;
+  for (int64_t base = wave * 64 * kUnroll; base < nchunk; base += nwaves * 64 * kUnroll) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t q = base + k * 64 + lane;
+      v[k] = q < nchunk ? x[q] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      if (!RHT) {
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          m = max(m, (w[i] & 0x7FFFu) << 16);
+          m = max(m, w[i] & 0x7FFF0000u);
+        }
+      } else {
+        float y[8];
+        unpack8(v[k], y);
+        rht16_pair(y, lane & 1, signs);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
+      }
+    }
+  }
+  block_max_atomic(m, a0, a1);
+}
+
+// amax of x and of RHT(x^T): lane owns 8 columns; walks 16-row blocks.
+__global__ __launch_bounds__(256) void k_amax_tile_rht(const uint16_t* __restrict__ x, int64_t R,
+                                                       int64_t C, int gx, int rbs, uint32_t signs,
+                                                       float* amax_row, float* amax_col) {
+  const int bx = blockIdx.x % gx, by = blockIdx.x / gx;
+  const int64_t c0 = ((int64_t)bx * blockDim.x + threadIdx.x) * 8;
+  uint32_t mr = 0, mc = 0;
+  if (c0 < C) {
+    for (int k = 0; k < rbs; ++k) {
+      const int64_t r0 = ((int64_t)by * rbs + k) * 16;
+      if (r0 >= R) break;
+      uint4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * C + c0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float y[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = tile_elem(v[i], j);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mr = max(mr, absbits(y[i]));
+        rht16(y, signs);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mc = max(mc, absbits(y[i]));
+      }
+    }
+  }
+  block_max_atomic(mr, amax_row, nullptr);
+  block_max_atomic(mc, amax_col, nullptr);
+}
+
+// ---------------------------------------------------------------- rowwise encoder
+
+template <int FMT, bool SR, bool RHT>
+__global__ __launch_bounds__(256) void k_quant_flat(const uint4* __restrict__ x, int64_t nchunk,
+                                                    const float* __restrict__ amax, uint32_t signs,
+                                                    uint64_t seed, uint32_t offset,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const float s_enc = FMT == kNVFP4 ? nvfp4_s_enc(*amax) : 0.0f;
+  for (int64_t base = wave * 64 * kUnroll; base < nchunk; base += nwaves * 64 * kUnroll) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t q = base + k * 64 + lane;
+      v[k] = q < nchunk ? x[q] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t q = base + k * 64 + lane;
+      float y[8];
+      unpack8(v[k], y);
+      if (RHT) rht16_pair(y, lane & 1, signs);
+      uint32_t m = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
+      m = max(m, dpp_xor1(m));
+      if (FMT != kNVFP4) m = max(m, dpp_xor2(m));
+      const float a_b = u2f(m);
+      uint32_t scode;
+      float mult;
+      if (FMT == kNVFP4) {
+        const BlockScale bs = nvfp4_block_scale(a_b, s_enc);
+        scode = bs.code;
+        mult = bs.enc;
+      } else {
+        const int e = mx_exponent(a_b, FMT == kMXFP4 ? 2 : 8);
+        scode = (uint32_t)(e + 127);
+        mult = exp2_neg(e);
+      }
+      float v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v8[e] = y[e] * mult;
+      if (q < nchunk) {
+        if (FMT == kMXFP8) {
+          reinterpret_cast<uint2*>(codes)[q] = encode8_fp8(v8);
+        } else {
+          R16x8 rnd{};
+          if (SR) rnd = sr_words((uint64_t)q, seed, offset, 0u);
+          reinterpret_cast<uint32_t*>(codes)[q] = encode8_fp4<SR>(v8, rnd);
+        }
+        if (FMT == kNVFP4) {
+          if ((lane & 1) == 0) scales[q >> 1] = (uint8_t)scode;
+        } else {
+          if ((lane & 3) == 0) scales[q >> 2] = (uint8_t)scode;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- row + column encoder
+
+// One lane owns columns [c0, c0+8) and walks `rbs` blocks of BLK rows.
+//  row output : per row, this lane's 8 values; the block spans BLK/8 lanes.
+//  col output : per column, the BLK values of this lane's registers.
+//  TWO_D      : one 16x16 tile scale for both orientations (NVFP4 only).
+template <int FMT, bool SR, bool RHT, bool TWO_D>
+__global__ __launch_bounds__(64) void k_quant_tile(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int gx, int rbs, int do_row, int do_col,
+    const float* __restrict__ amax_row, const float* __restrict__ amax_col, uint32_t signs,
+    uint64_t seed, uint32_t offset, uint8_t* __restrict__ codes_row,
+    uint8_t* __restrict__ scales_row, uint8_t* __restrict__ codes_col,
+    uint8_t* __restrict__ scales_col) {
+  constexpr int BLK = FMT == kNVFP4 ? 16 : 32;
+  constexpr int EMAX = FMT == kMXFP4 ? 2 : 8;
+  const int bx = blockIdx.x % gx, by = blockIdx.x / gx;
+  const int lane = threadIdx.x;
+  const int64_t c0 = ((int64_t)bx * 64 + lane) * 8;
+  if (c0 >= C) return;                       // whole lane groups leave together (C % BLK == 0)
+  float s_enc_row = 0.0f, s_enc_col = 0.0f;
+  if (FMT == kNVFP4) {
+    if (do_row) s_enc_row = nvfp4_s_enc(*amax_row);
+    if (do_col) s_enc_col = nvfp4_s_enc(*amax_col);
+  }
+  for (int k = 0; k < rbs; ++k) {
+    const int64_t r0 = ((int64_t)by * rbs + k) * BLK;
+    if (r0 >= R) break;
+    uint4 v[BLK];
+#pragma unroll
+    for (int i = 0; i < BLK; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * C + c0);
+
+    BlockScale tile{};
+    if (TWO_D) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) {
+        float y[8];
+        unpack8(v[i], y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
+      }
+      m = max(m, dpp_xor1(m));
+      tile = nvfp4_block_scale(u2f(m), do_row ? s_enc_row : s_enc_col);
+    }
+
+    if (do_row) {
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) {
+        const int64_t r = r0 + i;
+        float y[8];
+        unpack8(v[i], y);
+        uint32_t scode;
+        float mult;
+        if (TWO_D) {
+          scode = tile.code;
+          mult = tile.enc;
+        } else {
+          uint32_t m = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
+          m = max(m, dpp_xor1(m));
+          if (FMT != kNVFP4) m = max(m, dpp_xor2(m));
+          if (FMT == kNVFP4) {
+            const BlockScale bs = nvfp4_block_scale(u2f(m), s_enc_row);
+            scode = bs.code;
+            mult = bs.enc;
+          } else {
+            const int e = mx_exponent(u2f(m), EMAX);
+            scode = (uint32_t)(e + 127);
+            mult = exp2_neg(e);
+          }
+        }
+        float v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = y[e] * mult;
+        const int64_t flat = r * C + c0;                 // element index of the chunk
+        if (FMT == kMXFP8) {
+          reinterpret_cast<uint2*>(codes_row)[flat >> 3] = encode8_fp8(v8);
+        } else {
+          R16x8 rnd{};
+          if (SR) rnd = sr_words((uint64_t)(flat >> 3), seed, offset, 0u);
+          reinterpret_cast<uint32_t*>(codes_row)[flat >> 3] = encode8_fp4<SR>(v8, rnd);
+        }
+        if ((lane & (BLK / 8 - 1)) == 0) scales_row[flat / BLK] = (uint8_t)scode;
+      }
+    }
+
+    if (do_col) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t c = c0 + j;
+        float y[BLK];
+#pragma unroll
+        for (int i = 0; i < BLK; ++i) y[i] = tile_elem(v[i], j);
+        if (RHT) {
+          float (&y16)[16] = *reinterpret_cast<float(*)[16]>(&y[0]);
+          rht16(y16, signs);
+        }
+        uint32_t scode;
+        float mult;
+        if (TWO_D) {
+          scode = tile.code;
+          mult = tile.enc;
+        } else {
+          uint32_t m = 0;
+#pragma unroll
+          for (int i = 0; i < BLK; ++i) m = max(m, absbits(y[i]));
+          if (FMT == kNVFP4) {
+            const BlockScale bs = nvfp4_block_scale(u2f(m), s_enc_col);
+            scode = bs.code;
+            mult = bs.enc;
+          } else {
+            const int e = mx_exponent(u2f(m), EMAX);
+            scode = (uint32_t)(e + 127);
+            mult = exp2_neg(e);
+          }
+        }
+        const int64_t flat = c * R + r0;                 // element index in the [C, R] output
+#pragma unroll
+        for (int h = 0; h < BLK / 8; ++h) {
+          float v8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v8[e] = y[8 * h + e] * mult;
+          const int64_t grp = (flat >> 3) + h;
+          if (FMT == kMXFP8) {
+            reinterpret_cast<uint2*>(codes_col)[grp] = encode8_fp8(v8);
+          } else {
+            R16x8 rnd{};
+            if (SR) rnd = sr_words((uint64_t)grp, seed, offset, 1u);
+            reinterpret_cast<uint32_t*>(codes_col)[grp] = encode8_fp4<SR>(v8, rnd);
+          }
+        }
+        scales_col[flat / BLK] = (uint8_t)scode;
+      }
+    }
+  }
+}
+
+// Row-blocks per lane: as many as keeps >= 4096 waves in flight (up to 16).
+int pick_rbs(int64_t nrowblocks, int64_t waves_x) {
+  int rbs = 16;
+  while (rbs > 1 && ((nrowblocks + rbs - 1) / rbs) * waves_x < 4096) rbs >>= 1;
+  return rbs;
+}
+
+int64_t flat_grid(int64_t nchunk) {
+  const int64_t per_block = 256 * kUnroll;        // chunks per block per trip
+  int64_t g = (nchunk + per_block - 1) / per_block;
+  const int64_t cap = 256 * 32;                   // grid-stride beyond 32 blocks per CU
+  return g < 1 ? 1 : (g > cap ? cap : g);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_zero_amax(float* a, float* b, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_amax, dim3(1), dim3(64), 0, s, a, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_amax(const float* src, float* dst, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_amax, dim3(1), dim3(64), 0, s, src, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_flat(const void* x, int64_t nchunk, bool rht, uint32_t signs, float* a0,
+                            float* a1, hipStream_t s) {
+  const dim3 grid((unsigned)flat_grid(nchunk)), block(256);
+  const uint4* xp = static_cast<const uint4*>(x);
+  if (rht)
+    hipLaunchKernelGGL(k_amax_flat<true>, grid, block, 0, s, xp, nchunk, signs, a0, a1);
+  else
+    hipLaunchKernelGGL(k_amax_flat<false>, grid, block, 0, s, xp, nchunk, signs, a0, a1);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_tile_rht(const void* x, int64_t R, int64_t C, uint32_t signs,
+                                float* amax_row, float* amax_col, hipStream_t s) {
+  const int64_t lanes = C / 8;
+  const int gx = (int)((lanes + 255) / 256);
+  const int64_t nrb = R / 16;
+  const int rbs = pick_rbs(nrb, (lanes + 63) / 64);
+  const int64_t gy = (nrb + rbs - 1) / rbs;
+  hipLaunchKernelGGL(k_amax_tile_rht, dim3((unsigned)(gx * gy)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), R, C, gx, rbs, signs, amax_row, amax_col);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_flat(Fmt fmt, bool sr, bool rht, const void* x, int64_t nchunk,
+                             const float* amax, uint32_t signs, uint64_t seed, uint32_t offset,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const dim3 grid((unsigned)flat_grid(nchunk)), block(256);
+  const uint4* xp = static_cast<const uint4*>(x);
+#define BSQ_FLAT(F, S, H)                                                                  \
+  hipLaunchKernelGGL((k_quant_flat<F, S, H>), grid, block, 0, s, xp, nchunk, amax, signs, \
+                     seed, offset, codes, scales)
+  if (fmt == kNVFP4) {
+    if (sr) {
+      if (rht) BSQ_FLAT(kNVFP4, true, true); else BSQ_FLAT(kNVFP4, true, false);
+    } else {
+      if (rht) BSQ_FLAT(kNVFP4, false, true); else BSQ_FLAT(kNVFP4, false, false);
+    }
+  } else if (fmt == kMXFP4) {
+    if (sr) BSQ_FLAT(kMXFP4, true, false); else BSQ_FLAT(kMXFP4, false, false);
+  } else {
+    BSQ_FLAT(kMXFP8, false, false);
+  }
+#undef BSQ_FLAT
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tile(Fmt fmt, bool sr, bool rht_col, bool two_d, const void* x,
+                             int64_t R, int64_t C, bool do_row, bool do_col,
+                             const float* amax_row, const float* amax_col, uint32_t signs,
+                             uint64_t seed, uint32_t offset, uint8_t* codes_row,
+                             uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                             hipStream_t s) {
+  const int blk = fmt == kNVFP4 ? 16 : 32;
+  const int64_t lanes = C / 8;
+  const int gx = (int)((lanes + 63) / 64);
+  const int64_t nrb = R / blk;
+  const int rbs = pick_rbs(nrb, gx);
+  const int64_t gy = (nrb + rbs - 1) / rbs;
+  const dim3 grid((unsigned)(gx * gy)), block(64);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const int dr = do_row ? 1 : 0, dc = do_col ? 1 : 0;
+#define BSQ_TILE(F, S, H, D)                                                                  \
+  hipLaunchKernelGGL((k_quant_tile<F, S, H, D>), grid, block, 0, s, xp, R, C, gx, rbs, dr, dc, \
+                     amax_row, amax_col, signs, seed, offset, codes_row, scales_row, codes_col, \
+                     scales_col)
+  if (fmt == kNVFP4) {
+    if (two_d) {
+      BSQ_TILE(kNVFP4, false, false, true);
+    } else if (sr) {
+      if (rht_col) BSQ_TILE(kNVFP4, true, true, false); else BSQ_TILE(kNVFP4, true, false, false);
+    } else {
+      if (rht_col) BSQ_TILE(kNVFP4, false, true, false); else BSQ_TILE(kNVFP4, false, false, false);
+    }
+  } else if (fmt == kMXFP4) {
+    if (sr) BSQ_TILE(kMXFP4, true, false, false); else BSQ_TILE(kMXFP4, false, false, false);
+  } else {
+    BSQ_TILE(kMXFP8, false, false, false);
+  }
+#undef BSQ_TILE
+  return hipGetLastError();
+}
+
+}  // namespace bsq

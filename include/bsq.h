@@ -1,0 +1,171 @@
+/*
+ * bsq.h -- block-scaled quantize + GEMM for MI355X (gfx950).  C ABI.
+ *
+ * What is computed (source pages):
+ *  - NVFP4 pretraining post, section "NVFP4 pretraining recipe":
+ *      ingredient 1  16-element micro-blocks (1x16) along the reduction dim;
+ *      ingredient 2  E4M3 block scale factors under a per-tensor FP32 scale;
+ *      ingredient 3  16-point Random Hadamard Transform on WGRAD inputs only;
+ *      ingredient 4  16x16 2D weight scaling, so FPROP and the transposed
+ *                    DGRAD see identical values;
+ *      ingredient 5  round-to-nearest-even for weights/activations,
+ *                    stochastic rounding for gradients;
+ *    and the data-flow paragraph after Figure 1: the FPROP, DGRAD and WGRAD
+ *    GEMMs consume NVFP4 operands and emit BF16.
+ *  - HN page opcode84 (Triton on Blackwell quote, OCP MX spec link): MXFP8
+ *    (E4M3 elements) and MXFP4 (E2M1 elements) with one E8M0 power-of-two
+ *    scale per 32 elements, applied inside the matrix unit.
+ *
+ * Numerical definitions (bit-exact contract of the quantizers):
+ *  - E2M1 magnitudes {0,0.5,1,1.5,2,3,4,6}, ties to the even code, saturate
+ *    at 6; sign bit 0x8 kept (-0 -> 0x8).  Two codes per byte, the element
+ *    with the even index in the low nibble.
+ *  - E4M3 = OCP E4M3FN, subnormals kept, saturate at 448 (0x7E).
+ *  - NVFP4 per-tensor scale: amax = max|x| (of the transformed values when the
+ *    RHT applies); s_enc = 2688/amax (FP32; 1 if amax == 0; <= FLT_MAX);
+ *    s_dec = 1/s_enc.  Block: sf = (a_b/6)*s_enc; S = E4M3(sf);
+ *    enc = S ? min(s_enc/S, FLT_MAX) : 0; code = E2M1(x*enc).  FP32 IEEE
+ *    RNE at every step, no fused multiply-add.
+ *  - MX scale: e = floor(log2 a_b) - emax (emax 2 for E2M1, 8 for E4M3),
+ *    -127 for an all-zero block, clamped to [-127,127], stored as e+127;
+ *    element = E2M1/E4M3(x * 2^-e).
+ *  - RHT: for each aligned 16-chunk y along the blocked dim: negate y_i where
+ *    bit i of rht_signs is set, then butterflies h = 1,2,4,8
+ *    (y_i, y_i+h) <- (y_i + y_i+h, y_i - y_i+h), then y *= 0.25 (FP32).
+ *  - Stochastic rounding: element (r,c) of an output of shape [R',C'] in its
+ *    own orientation has idx = r*C' + c; Philox4x32-10 (Salmon et al., SC'11)
+ *    with key (seed lo, seed hi) and counter (lo(idx>>3), hi(idx>>3), offset,
+ *    stream) gives 8 16-bit halves, the element takes half idx&7 (word
+ *    (idx&7)>>1, low half first); stream 0 = rowwise, 1 = columnwise.  With
+ *    lo <= |v| < hi the neighbouring E2M1 points, round up iff
+ *    r16 < floor((|v|-lo)/(hi-lo) * 65536); |v| >= 6 -> 6.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, and
+ *    must be 16-byte aligned.  `x` is BF16.  The caller allocates every
+ *    buffer; the library never allocates, frees or retains device memory and
+ *    keeps no state between calls.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronizes the host.
+ *  - Argument errors are detected before anything is launched: the call
+ *    returns BSQ_EINVAL / BSQ_EUNSUPPORTED and no output is touched.  A launch
+ *    failure returns BSQ_EHIP.  No exception crosses the ABI.
+ *  - Inputs must be finite; NaN/Inf inputs give unspecified codes but never a
+ *    fault.
+ *  - Sizes: rows, cols, M, N, K >= 0; a zero-size call returns BSQ_OK and
+ *    launches nothing except that amax outputs are set to 0.
+ */
+#ifndef BSQ_H
+#define BSQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSQ_OK = 0,
+  BSQ_EINVAL = 1,        /* null pointer, bad size, misalignment */
+  BSQ_EUNSUPPORTED = 2,  /* combination the recipe does not define */
+  BSQ_EHIP = 3           /* HIP launch error */
+} bsq_status;
+
+typedef enum { BSQ_NVFP4 = 0, BSQ_MXFP4 = 1, BSQ_MXFP8 = 2 } bsq_format;
+typedef enum { BSQ_RNE = 0, BSQ_SR = 1 } bsq_rounding;
+
+/*
+ * Rowwise NVFP4 of x[rows, cols] (BF16), blocks along cols.
+ * Recipe ingredients 1, 2, 4, 5 (and 3 when rht != 0).
+ *   block_rows : 1 (1x16 blocks) or 16 (16x16 tiles, rows % 16 == 0; the tile
+ *                scale is written to each of its 16 rows).
+ *   rnd        : BSQ_RNE or BSQ_SR (SR uses stream 0); SR with block_rows 16
+ *                is BSQ_EUNSUPPORTED (it would break the transpose invariant).
+ *   seed/offset: Philox key and counter word 2 for SR (ignored for RNE).
+ *   rht        : nonzero = apply the 16-point RHT along cols first (amax is then
+ *                taken over the transformed values); not with block_rows 16.
+ *   amax_in    : NULL, or a device FP32 amax to use instead of computing it.
+ *   codes      : out, uint8 [rows, cols/2], packed E2M1.
+ *   scales     : out, uint8 [rows, cols/16], E4M3 block scales.
+ *   amax_out   : out, device FP32 scalar: the amax used.  Required when
+ *                amax_in is NULL (it is the reduction's accumulator); may be
+ *                NULL otherwise.
+ * Requires cols % 16 == 0.
+ */
+bsq_status nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int block_rows,
+                          bsq_rounding rnd, uint64_t seed, uint32_t offset,
+                          int rht, uint16_t rht_signs, const float* amax_in,
+                          uint8_t* codes, uint8_t* scales, float* amax_out,
+                          void* stream);
+
+/*
+ * Rowwise MXFP4 (fmt BSQ_MXFP4, E2M1 elements) or MXFP8 (BSQ_MXFP8, E4M3
+ * elements) of x[rows, cols] with one E8M0 scale per 32 elements along cols.
+ * HN page opcode84 (MX formats; OCP MX spec).
+ *   rnd    : BSQ_RNE, or BSQ_SR for MXFP4 only (stream 0).
+ *   codes  : out, uint8 [rows, cols/2] (MXFP4) or [rows, cols] (MXFP8).
+ *   scales : out, uint8 [rows, cols/32], E8M0.
+ * Requires cols % 32 == 0.
+ */
+bsq_status mx_quantize(const void* x, int64_t rows, int64_t cols, bsq_format fmt,
+                       bsq_rounding rnd, uint64_t seed, uint32_t offset,
+                       uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Both orientations from one read of x[rows, cols]:
+ *   row = quantize(x)    -> codes_row [rows, cols/2 or cols], scales_row [rows, cols/B]
+ *   col = quantize(x^T)  -> codes_col [cols, rows/2 or rows], scales_col [cols, rows/B]
+ * B = 16 (NVFP4) or 32 (MX).  Recipe: ingredient 4 (the transposed DGRAD
+ * operand of 2D-scaled weights), ingredient 3 (WGRAD operands are quantized
+ * along tokens, with the RHT), data-flow paragraph.
+ *   fmt        : BSQ_NVFP4, BSQ_MXFP4 or BSQ_MXFP8.
+ *   block_rows : 1, or 16 for NVFP4 2D tiles (then row and col codes are the
+ *                same values transposed and both scale arrays hold the same
+ *                tile scales).
+ *   rnd        : RNE or SR (SR: rowwise stream 0, columnwise stream 1); not SR
+ *                with 2D tiles or MXFP8.
+ *   rht_col    : nonzero = RHT along rows (the blocked dim of x^T) for the col
+ *                output only; NVFP4 1x16 only.
+ *   amax_row / amax_col : out, device FP32 (NVFP4 only; ignored for MX).
+ *                amax_row = max|x|; amax_col = max|RHT(x^T)| with rht_col,
+ *                else equal to amax_row.
+ * Either triple (codes_row, scales_row, amax_row) or (codes_col, scales_col,
+ * amax_col) may be all-NULL to skip that orientation (not both).
+ * Requires rows % 16 == 0 and cols % 16 == 0 (NVFP4) or rows % 32 == 0 and
+ * cols % 32 == 0 (MX).
+ */
+bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_format fmt,
+                              int block_rows, bsq_rounding rnd, uint64_t seed, uint32_t offset,
+                              int rht_col, uint16_t rht_signs,
+                              uint8_t* codes_row, uint8_t* scales_row, float* amax_row,
+                              uint8_t* codes_col, uint8_t* scales_col, float* amax_col,
+                              void* stream);
+
+/*
+ * C[M, N] (BF16, row-major, row stride ldc >= N elements) =
+ *     alpha * sum_k deq(A)[m, k] * deq(B)[n, k]
+ * with A [M, K] and B [N, K] both K-major (quantized along K), FP32
+ * accumulation and one BF16 round-to-nearest-even at the end.  Data-flow
+ * paragraph: FPROP (A = X rowwise, B = W rowwise 2D), DGRAD (A = dY rowwise,
+ * B = W columnwise 2D), WGRAD (A = dY columnwise, B = X columnwise, K = tokens).
+ *   NVFP4: codes [M, K/2] + E4M3 scales [M, K/16] per operand and a device
+ *          FP32 amax per operand; alpha = s_dec(a_amax) * s_dec(b_amax).
+ *          Requires K % 16 == 0.
+ *   MXFP4: codes [M, K/2], MXFP8: codes [M, K]; E8M0 scales [M, K/32];
+ *          a_amax and b_amax are ignored (may be NULL); alpha = 1.
+ *          Requires K % 32 == 0.
+ * M and N may be any value >= 0.  C must not alias any input.
+ */
+bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K,
+                   const uint8_t* a_codes, const uint8_t* a_scales, const float* a_amax,
+                   const uint8_t* b_codes, const uint8_t* b_scales, const float* b_amax,
+                   void* c, int64_t ldc, void* stream);
+
+/* Static, human-readable name of a status code; host-side, thread-safe. */
+const char* bsq_status_string(bsq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSQ_H */

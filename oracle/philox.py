@@ -72,8 +72,11 @@ def sr_random16(idx, seed, offset, stream):
     return ((w >> (np.uint32(16) * half)) & np.uint32(0xFFFF)).astype(np.uint32)
 
 
-def sr_random16_grid(rows, cols, seed, offset, stream):
-    """16-bit random words for a whole [rows, cols] output in its own orientation."""
-    idx = (np.arange(rows, dtype=np.uint64)[:, None] * np.uint64(cols)
-           + np.arange(cols, dtype=np.uint64)[None, :])
+def sr_random16_grid(rows, cols, seed, offset, stream, row_ids=None):
+    """16-bit random words for a [rows, cols] output in its own orientation.
+
+    row_ids (optional) gives the global row index of each of the `rows` rows
+    when only a subset of the output's rows is being computed."""
+    r = np.arange(rows, dtype=np.uint64) if row_ids is None else np.asarray(row_ids, dtype=np.uint64)
+    idx = r[:, None] * np.uint64(cols) + np.arange(cols, dtype=np.uint64)[None, :]
     return sr_random16(idx, seed, offset, stream)

@@ -40,7 +40,7 @@ import numpy as np
 
 from . import formats as F
 from .philox import sr_random16_grid, STREAM_ROW, STREAM_COL
-from .rht import rht_along_rows
+from .rht import rht_along_rows, rht16
 
 NVFP4_BLOCK = 16
 MX_BLOCK = 32
@@ -110,12 +110,15 @@ def nvfp4_encode_blocks(y, block_amax, s_enc, rnd, r16=None):
 
 
 def nvfp4_quantize(x, block_rows=1, rnd="rne", seed=0, offset=0, stream=STREAM_ROW,
-                   rht=False, rht_signs=0, amax=None):
+                   rht=False, rht_signs=0, amax=None, row_ids=None):
     """Rowwise NVFP4 of x [R, C] (blocks along C).
 
     Returns (codes uint8 [R, C/2], scales uint8 [R, C/16], amax float32).
     With rht=True the RHT is applied along C first and amax is taken over the
     transformed values.  `amax` may be supplied (it is then used as given).
+    row_ids: when x holds only some rows of a larger tensor (whole 16-row tiles
+    for block_rows=16), their global row indices; they place the stochastic
+    rounding stream.  amax must then be given.
     """
     y = as_f32(x)
     R, C = y.shape
@@ -127,9 +130,26 @@ def nvfp4_quantize(x, block_rows=1, rnd="rne", seed=0, offset=0, stream=STREAM_R
     if amax is None:
         amax = tensor_amax(y)
     s_enc = nvfp4_scale_enc(amax)
-    r16 = sr_random16_grid(R, C, seed, offset, stream) if rnd == "sr" else None
+    if row_ids is not None:
+        assert amax is not None and len(row_ids) == R
+    r16 = sr_random16_grid(R, C, seed, offset, stream, row_ids) if rnd == "sr" else None
     codes, S = nvfp4_encode_blocks(y, nvfp4_block_amax(y, block_rows), s_enc, rnd, r16)
     return codes, S, np.float32(amax)
+
+
+def tensor_amax_rht_cols(x, rht_signs, chunk_rows=2048):
+    """max |RHT(x^T)| over a whole tensor x [R, C]: the RHT runs along R (the
+    blocked dimension of x^T).  Same definition as tensor_amax(rht_along_rows(x^T)),
+    evaluated over 16-row slabs of x at a time to bound memory."""
+    R, C = x.shape
+    assert R % 16 == 0 and chunk_rows % 16 == 0
+    m = np.float32(0.0)
+    for r0 in range(0, R, chunk_rows):
+        y = as_f32(x[r0:r0 + chunk_rows])
+        n = y.shape[0] // 16
+        chunks = np.ascontiguousarray(y.reshape(n, 16, C).transpose(0, 2, 1))   # [n, C, 16]
+        m = max(m, tensor_amax(rht16(chunks, rht_signs)))
+    return np.float32(m)
 
 
 # --------------------------------------------------------------------------
@@ -148,7 +168,7 @@ def mx_scale_exponent(block_amax, fmt):
     return np.clip(e, -127, 127)
 
 
-def mx_quantize(x, fmt="mxfp4", rnd="rne", seed=0, offset=0, stream=STREAM_ROW):
+def mx_quantize(x, fmt="mxfp4", rnd="rne", seed=0, offset=0, stream=STREAM_ROW, row_ids=None):
     """Rowwise MX quantization of x [R, C] (blocks of 32 along C).
 
     Returns (codes, scales): codes uint8 [R, C/2] (mxfp4) or [R, C] (mxfp8),
@@ -164,7 +184,7 @@ def mx_quantize(x, fmt="mxfp4", rnd="rne", seed=0, offset=0, stream=STREAM_ROW):
         if rnd == "rne":
             codes = F.e2m1_encode_rne(v)
         else:
-            codes = F.e2m1_encode_sr(v, sr_random16_grid(R, C, seed, offset, stream))
+            codes = F.e2m1_encode_sr(v, sr_random16_grid(R, C, seed, offset, stream, row_ids))
         codes = F.pack_e2m1(codes)
     else:
         assert rnd == "rne"

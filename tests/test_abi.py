@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: libbsq.so loads, exports exactly the entry
+points include/bsq.h declares, and rejects invalid arguments before touching
+the device (argument validation returns without any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_quantized_gemm_amd as bsq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bsq.LIB_PATH),
+                                reason="libbsq.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == set(bsq.ABI_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(bsq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for st, word in ((0, "BSQ_OK"), (1, "EINVAL"), (2, "EUNSUPPORTED"), (3, "EHIP")):
+        assert word in bsq.status_string(st)
+    assert "UNKNOWN" in bsq.status_string(99)
+
+
+FAKE = 0x100000   # a 16-byte aligned non-null address that is never dereferenced
+
+
+def _nv(**kw):
+    a = dict(x=FAKE, rows=32, cols=32, block_rows=1, rnd=0, seed=0, offset=0, rht=0, signs=0,
+             amax_in=None, codes=FAKE, scales=FAKE, amax_out=FAKE)
+    a.update(kw)
+    return bsq.lib().nvfp4_quantize(a["x"], a["rows"], a["cols"], a["block_rows"], a["rnd"],
+                                    a["seed"], a["offset"], a["rht"], a["signs"], a["amax_in"],
+                                    a["codes"], a["scales"], a["amax_out"], None)
+
+
+def test_nvfp4_quantize_argument_errors():
+    assert _nv(cols=24) == bsq.BSQ_EINVAL                 # cols % 16
+    assert _nv(rows=-1) == bsq.BSQ_EINVAL
+    assert _nv(block_rows=4) == bsq.BSQ_EINVAL
+    assert _nv(block_rows=16, rows=24) == bsq.BSQ_EINVAL  # 2D needs rows % 16
+    assert _nv(amax_out=None) == bsq.BSQ_EINVAL           # no amax source
+    assert _nv(x=None) == bsq.BSQ_EINVAL
+    assert _nv(codes=FAKE + 4) == bsq.BSQ_EINVAL          # misaligned
+    assert _nv(rnd=7) == bsq.BSQ_EINVAL
+    assert _nv(block_rows=16, rnd=1) == bsq.BSQ_EUNSUPPORTED
+    assert _nv(block_rows=16, rht=1) == bsq.BSQ_EUNSUPPORTED
+
+
+def _mx(fmt=1, rows=32, cols=64, rnd=0, x=FAKE, codes=FAKE, scales=FAKE):
+    return bsq.lib().mx_quantize(x, rows, cols, fmt, rnd, 0, 0, codes, scales, None)
+
+
+def test_mx_quantize_argument_errors():
+    assert _mx(cols=48) == bsq.BSQ_EINVAL
+    assert _mx(fmt=0) == bsq.BSQ_EUNSUPPORTED
+    assert _mx(fmt=5) == bsq.BSQ_EINVAL
+    assert _mx(fmt=2, rnd=1) == bsq.BSQ_EUNSUPPORTED
+    assert _mx(scales=None) == bsq.BSQ_EINVAL
+    assert _mx(rows=0) == bsq.BSQ_OK                      # empty: nothing to launch
+
+
+def _qt(fmt=0, rows=32, cols=32, block_rows=1, rnd=0, rht=0, row=True, col=True, x=FAKE):
+    r = FAKE if row else None
+    c = FAKE if col else None
+    return bsq.lib().quantize_transpose(x, rows, cols, fmt, block_rows, rnd, 0, 0, rht, 0,
+                                        r, r, r, c, c, c, None)
+
+
+def test_quantize_transpose_argument_errors():
+    assert _qt(rows=24) == bsq.BSQ_EINVAL                 # rows % 16
+    assert _qt(fmt=1, rows=48) == bsq.BSQ_EINVAL          # MX needs rows % 32
+    assert _qt(row=False, col=False) == bsq.BSQ_EINVAL
+    assert _qt(fmt=1, rht=1) == bsq.BSQ_EUNSUPPORTED
+    assert _qt(fmt=1, block_rows=16) == bsq.BSQ_EUNSUPPORTED
+    assert _qt(fmt=2, rnd=1) == bsq.BSQ_EUNSUPPORTED
+    assert _qt(block_rows=16, rnd=1) == bsq.BSQ_EUNSUPPORTED
+    assert _qt(block_rows=16, rht=1) == bsq.BSQ_EUNSUPPORTED
+    assert _qt(x=None) == bsq.BSQ_EINVAL
+    L = bsq.lib()
+    # partial triple: codes given, scales missing
+    assert L.quantize_transpose(FAKE, 32, 32, 0, 1, 0, 0, 0, 0, 0, FAKE, None, FAKE,
+                                None, None, None, None) == bsq.BSQ_EINVAL
+
+
+def test_bs_gemm_argument_errors():
+    L = bsq.lib()
+    g = lambda fmt=0, M=16, N=16, K=32, ldc=16, a=FAKE, amax=FAKE, c=FAKE: L.bs_gemm(
+        fmt, M, N, K, a, FAKE, amax, FAKE, FAKE, amax, c, ldc, None)
+    assert g(K=24) == bsq.BSQ_EINVAL                      # NVFP4 K % 16
+    assert g(fmt=1, K=48) == bsq.BSQ_EINVAL               # MX K % 32
+    assert g(ldc=8) == bsq.BSQ_EINVAL                     # ldc < N
+    assert g(a=None) == bsq.BSQ_EINVAL
+    assert g(amax=None) == bsq.BSQ_EINVAL                 # NVFP4 needs both amax
+    assert g(c=None) == bsq.BSQ_EINVAL
+    assert g(fmt=9) == bsq.BSQ_EINVAL
+    assert g(M=0) == bsq.BSQ_OK and g(N=0) == bsq.BSQ_OK  # empty output: nothing to launch
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(bsq, "_lib", None)
+    monkeypatch.setattr(bsq, "LIB_PATH", "/nonexistent/libbsq.so")
+    with pytest.raises(RuntimeError):
+        bsq.lib()

@@ -218,3 +218,14 @@ def test_quantize_transpose_col_equals_rowwise_of_transpose():
     assert r["col_amax"] == a2
     r1, s1, a1 = Q.nvfp4_quantize(x, 1, "sr", 9, 3, stream=0)
     assert np.array_equal(r["row_codes"], r1) and r["row_amax"] == a1
+
+
+def test_row_subset_matches_full_and_chunked_rht_amax():
+    x = bf16_bits(synth.bf16_tensor((64, 96), 18))
+    full = Q.quantize_transpose(x, "nvfp4", 1, "sr", seed=4, offset=2, rht_col=True, rht_signs=0x3C5A)
+    ids = np.array([3, 17, 50, 95])
+    xt = np.ascontiguousarray(x.T)[ids]
+    c, s, _ = Q.nvfp4_quantize(xt, 1, "sr", 4, 2, stream=1, rht=True, rht_signs=0x3C5A,
+                               amax=full["col_amax"], row_ids=ids)
+    assert np.array_equal(c, full["col_codes"][ids]) and np.array_equal(s, full["col_scales"][ids])
+    assert Q.tensor_amax_rht_cols(x, 0x3C5A, chunk_rows=32) == full["col_amax"]
