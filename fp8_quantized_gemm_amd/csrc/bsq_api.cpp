@@ -102,22 +102,23 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
   const bool do_row = codes_row || scales_row || (nv && amax_row);
   const bool do_col = codes_col || scales_col || (nv && amax_col);
   if (!do_row && !do_col) return BSQ_EINVAL;
+  if (!nv && (block_rows == 16 || rht_col)) return BSQ_EUNSUPPORTED;
+  if (fmt == BSQ_MXFP8 && rnd == BSQ_SR) return BSQ_EUNSUPPORTED;
+  if (block_rows == 16 && (rnd == BSQ_SR || rht_col)) return BSQ_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (rows * cols == 0) {                      // empty tensor: only the amax outputs are defined
+    if (nv && (!aligned4(amax_row) || !aligned4(amax_col))) return BSQ_EINVAL;
+    if (nv) return hip_status(bsq::launch_zero_amax(amax_row, amax_col, s));
+    return BSQ_OK;
+  }
   if (do_row && (!codes_row || !scales_row || (nv && !amax_row))) return BSQ_EINVAL;
   if (do_col && (!codes_col || !scales_col || (nv && !amax_col))) return BSQ_EINVAL;
   if (!aligned16_or_null(codes_row) || !aligned16_or_null(scales_row) ||
       !aligned16_or_null(codes_col) || !aligned16_or_null(scales_col))
     return BSQ_EINVAL;
   if (nv && (!aligned4(amax_row) || !aligned4(amax_col))) return BSQ_EINVAL;
-  if (!nv && (block_rows == 16 || rht_col)) return BSQ_EUNSUPPORTED;
-  if (fmt == BSQ_MXFP8 && rnd == BSQ_SR) return BSQ_EUNSUPPORTED;
-  if (block_rows == 16 && (rnd == BSQ_SR || rht_col)) return BSQ_EUNSUPPORTED;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   float* ar = do_row ? amax_row : nullptr;
   float* ac = do_col ? amax_col : nullptr;
-  if (rows * cols == 0) {
-    if (nv) return hip_status(bsq::launch_zero_amax(ar, ac, s));
-    return BSQ_OK;
-  }
   if (!x || !aligned16(x)) return BSQ_EINVAL;
 
   hipError_t e;

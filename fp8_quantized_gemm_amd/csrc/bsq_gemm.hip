@@ -10,9 +10,10 @@
 //    from LDS straight into the MFMA.
 //  * NVFP4: the 16-element E4M3 block scale is not an MFMA scale type.  Each
 //    E2M1 value times an E4M3 scale has at most 6 significant bits and lies in
-//    [2^-10, 2688], so it is exact in BF16: the codes are expanded in
-//    registers to BF16 products and fed to v_mfma_f32_32x32x16_bf16 (FP32
-//    accumulate).  The per-tensor scales multiply the FP32 result once.
+//    [2^-10, 2688], so it is exact in FP16 (and BF16): the codes are expanded
+//    in registers to FP16 products (see dequant8) and fed to
+//    v_mfma_f32_32x32x16_f16 (FP32 accumulate).  The per-tensor scales multiply
+//    the FP32 result once.
 //
 // Tiling: 256x256 output tile per 512-thread block (8 waves as 2 x 4, each
 // wave 128 (M) x 64 (N) = 4 x 2 MFMA tiles of 32x32), K stage of 128
@@ -32,8 +33,8 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256, kBN = 256, kThreads = 512;
 
@@ -63,14 +64,34 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
 }
 
-// 8 E2M1 codes (one dword, element 2b in the low nibble of byte b) times a
-// float scale -> 8 BF16 values, exact.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
-  bf16x8 r;
+// Block scale S (E4M3 byte SEL of w) as the FP16 pair {S * 2^7, S * 2^7}
+// (exact: S * 2^7 lies in [2^-2, 57344]).
+template <int SEL>
+__device__ __forceinline__ halfx2 nvfp4_scale_pair(uint32_t w) {
+  const float s = e4m3_to_f32<SEL>(w) * 128.0f;
+  return __builtin_bit_cast(halfx2, __builtin_amdgcn_cvt_pkrtz(s, s));
+}
+
+// 8 E2M1 codes (nibble i = element i of one dword) times a block scale, as 8
+// FP16 values v * S * 2^-7 (exact), in the K order [0, 4, 1, 5, 2, 6, 3, 7].
+// E2M1 is a 1-sign / 2-exponent / 1-mantissa float: moving its magnitude bits
+// to FP16 bits 9..11 and its sign to bit 15 gives exactly v * 2^-14 (code 1,
+// 0.5, lands on the FP16 subnormal 0.5 * 2^-14).  Pairing nibbles i and i+4
+// in one dword makes both halves need the same shifts.  The packed FP16
+// multiply by S * 2^7 is exact: v * S has at most 6 significant bits, its
+// lowest bit is >= 2^-10, so v * S * 2^-7 is representable (FP16 denormals
+// are kept).  The MFMA products then carry 2^-14 per operand pair, undone in
+// the epilogue.
+__device__ __forceinline__ halfx8 dequant8(uint32_t w, halfx2 s2) {
+  const uint32_t d0 = ((w << 9) & 0x0E000E00u) | ((w << 12) & 0x80008000u);
+  const uint32_t d1 = ((w << 5) & 0x0E000E00u) | ((w << 8) & 0x80008000u);
+  const uint32_t d2 = ((w << 1) & 0x0E000E00u) | ((w << 4) & 0x80008000u);
+  const uint32_t d3 = ((w >> 3) & 0x0E000E00u) | (w & 0x80008000u);
+  const halfx2 p0 = __builtin_bit_cast(halfx2, d0) * s2;
+  const halfx2 p1 = __builtin_bit_cast(halfx2, d1) * s2;
+  const halfx2 p2 = __builtin_bit_cast(halfx2, d2) * s2;
+  const halfx2 p3 = __builtin_bit_cast(halfx2, d3) * s2;
+  halfx8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
@@ -250,6 +271,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
         scb[ni] = *reinterpret_cast<const uint32_t*>(LSb + (wn * 64 + ni * 32 + l32) * 8 + 4 * h);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {          // 16-byte reads: 4 K-steps each
+        halfx2 ssa[4][2], ssb[2][2];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          ssa[mi][0] = half == 0 ? nvfp4_scale_pair<0>(sca[mi]) : nvfp4_scale_pair<2>(sca[mi]);
+          ssa[mi][1] = half == 0 ? nvfp4_scale_pair<1>(sca[mi]) : nvfp4_scale_pair<3>(sca[mi]);
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          ssb[ni][0] = half == 0 ? nvfp4_scale_pair<0>(scb[ni]) : nvfp4_scale_pair<2>(scb[ni]);
+          ssb[ni][1] = half == 0 ? nvfp4_scale_pair<1>(scb[ni]) : nvfp4_scale_pair<3>(scb[ni]);
+        }
         uint4 ca[4], cb[2];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
@@ -262,71 +294,73 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           // K step (4*half + s) covers lane elements 8*(4*half+s) .. +7 -> scale byte 2*half + s/2
-          bf16x8 fa[4], fb[2];
+          halfx8 fa[4], fb[2];
 #pragma unroll
           for (int mi = 0; mi < 4; ++mi) {
             const uint32_t w = s == 0 ? ca[mi].x : s == 1 ? ca[mi].y : s == 2 ? ca[mi].z : ca[mi].w;
-            const float scl = half == 0 ? (s < 2 ? e4m3_to_f32<0>(sca[mi]) : e4m3_to_f32<1>(sca[mi]))
-                                        : (s < 2 ? e4m3_to_f32<2>(sca[mi]) : e4m3_to_f32<3>(sca[mi]));
-            fa[mi] = dequant8(w, scl);
+            fa[mi] = dequant8(w, s < 2 ? ssa[mi][0] : ssa[mi][1]);
           }
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni) {
             const uint32_t w = s == 0 ? cb[ni].x : s == 1 ? cb[ni].y : s == 2 ? cb[ni].z : cb[ni].w;
-            const float scl = half == 0 ? (s < 2 ? e4m3_to_f32<0>(scb[ni]) : e4m3_to_f32<1>(scb[ni]))
-                                        : (s < 2 ? e4m3_to_f32<2>(scb[ni]) : e4m3_to_f32<3>(scb[ni]));
-            fb[ni] = dequant8(w, scl);
+            fb[ni] = dequant8(w, s < 2 ? ssb[ni][0] : ssb[ni][1]);
           }
 #pragma unroll
           for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
         }
       }
     } else {
-      // MX: lane half h, step s uses the 32-element block h*STEPS + s of the stage
-      constexpr int EB = FMT == kMXFP8 ? 32 : 16;     // bytes per 32-element block
+      // MX operand layouts of v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 = two
+      // 32-element MX blocks per instruction; block b's E8M0 scale comes from
+      // lane half b):
+      //  * FP4: lane half h supplies one whole block (32 codes, 16 bytes); here
+      //    step s of the stage uses block h*STEPS + s for lane half h.
+      //  * FP8: bytes 0-15 of every lane belong to the first block of the
+      //    instruction and bytes 16-31 to the second, each block split over the
+      //    two lane halves; here step s uses blocks 2s and 2s+1, lane half h
+      //    taking elements [16h, 16h+16) of each.
       constexpr int FMTC = FMT == kMXFP8 ? 0 : 4;     // cbsz / blgp operand type
       uint32_t sca[4], scb[2];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        const uint8_t* p = LSa + (wm * 128 + mi * 32 + l32) * C::SB + h * C::STEPS;
-        sca[mi] = C::STEPS == 4 ? *reinterpret_cast<const uint32_t*>(p)
-                                : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+        const int row = wm * 128 + mi * 32 + l32;
+        sca[mi] = FMT == kMXFP8 ? (*reinterpret_cast<const uint32_t*>(LSa + row * 4) >> (8 * h))
+                                : *reinterpret_cast<const uint32_t*>(LSa + row * 8 + 4 * h);
       }
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
-        const uint8_t* p = LSb + (wn * 64 + ni * 32 + l32) * C::SB + h * C::STEPS;
-        scb[ni] = C::STEPS == 4 ? *reinterpret_cast<const uint32_t*>(p)
-                                : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+        const int row = wn * 64 + ni * 32 + l32;
+        scb[ni] = FMT == kMXFP8 ? (*reinterpret_cast<const uint32_t*>(LSb + row * 4) >> (8 * h))
+                                : *reinterpret_cast<const uint32_t*>(LSb + row * 8 + 4 * h);
       }
+      auto frag = [&](const uint8_t* base, int row, int s) {
+        const uint8_t* p = base + row * C::LDR;
+        uint4 lo, hi = make_uint4(0, 0, 0, 0);
+        if (FMT == kMXFP8) {
+          lo = *reinterpret_cast<const uint4*>(p + (2 * s) * 32 + 16 * h);
+          hi = *reinterpret_cast<const uint4*>(p + (2 * s + 1) * 32 + 16 * h);
+        } else {
+          lo = *reinterpret_cast<const uint4*>(p + (h * C::STEPS + s) * 16);
+        }
+        return intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
 #pragma unroll
       for (int s = 0; s < C::STEPS; ++s) {
+        const int sel = FMT == kMXFP8 ? 2 * s : s;    // scale byte of this lane's block
         intx8 fa[4], fb[2];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          const uint8_t* p = La + (wm * 128 + mi * 32 + l32) * C::LDR + (h * C::STEPS + s) * EB;
-          const uint4 lo = *reinterpret_cast<const uint4*>(p);
-          uint4 hi = make_uint4(0, 0, 0, 0);
-          if (EB == 32) hi = *reinterpret_cast<const uint4*>(p + 16);
-          fa[mi] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
+        for (int mi = 0; mi < 4; ++mi) fa[mi] = frag(La, wm * 128 + mi * 32 + l32, s);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const uint8_t* p = Lb + (wn * 64 + ni * 32 + l32) * C::LDR + (h * C::STEPS + s) * EB;
-          const uint4 lo = *reinterpret_cast<const uint4*>(p);
-          uint4 hi = make_uint4(0, 0, 0, 0);
-          if (EB == 32) hi = *reinterpret_cast<const uint4*>(p + 16);
-          fb[ni] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
+        for (int ni = 0; ni < 2; ++ni) fb[ni] = frag(Lb, wn * 64 + ni * 32 + l32, s);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = mfma_mx<FMTC>(s, fb[ni], fa[mi], acc[mi][ni], scb[ni], sca[mi]);
+            acc[mi][ni] = mfma_mx<FMTC>(sel, fb[ni], fa[mi], acc[mi][ni], scb[ni], sca[mi]);
         __builtin_amdgcn_sched_barrier(0);      // keep each step's fragments short-lived
       }
     }
@@ -341,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   // epilogue: alpha * acc -> BF16 (RNE).  Lane holds column m = l32 of D = C^T,
   // rows n = 8*(r/4) + 4*h + r%4 of each 32x32 tile.
   float alpha = 1.0f;
-  if (FMT == kNVFP4) alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax);
+  if (FMT == kNVFP4) alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax) * 16384.0f;   // undo 2^-7 per operand
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int64_t m = m0 + wm * 128 + mi * 32 + l32;
