@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsq.so")
 
-SOURCES = ["bsq_api.cpp", "bsq_quantize.hip", "bsq_gemm.hip"]
+SOURCES = ["bsq_api.cpp", "bsq_quantize.hip", "bsq_gemm.hip", "bsq_gemm_nvfp4.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -85,19 +85,59 @@ __device__ __forceinline__ float nvfp4_s_enc(float amax) {
   return fminf(2688.0f / amax, kFltMax);
 }
 
-// Block step: sf = (a_b / 6) * s_enc; S = E4M3(sf); enc = s_enc / S (0 if S == 0).
+// Correctly rounded a / 6 for a >= 0.  For a >= 2^-120 the quotient is a
+// normal float and one FMA correction step on a * RN(1/6) gives the IEEE
+// result (checked against IEEE division on every FP32 input on gfx950);
+// below that, plain IEEE division.
+__device__ __forceinline__ float div6(float a) {
+  if (a < 0x1p-120f) return a / 6.0f;
+  const float y = 1.0f / 6.0f;
+  const float q = a * y;
+  const float r = __builtin_fmaf(-q, 6.0f, a);
+  return __builtin_fmaf(r, y, q);
+}
+
+// E4M3 code (0..0x7E) of the block scale sf = (a_b / 6) * s_enc, RNE and
+// saturating at 448.  The hardware FP32 -> E4M3 convert rounds to nearest
+// even and agrees with e4m3_rne_mag on [0, 464) (checked exhaustively); the
+// clamp maps everything above 448 (reachable only with a caller-supplied
+// amax below the true one) to 448, as e4m3_rne_mag does.
+__device__ __forceinline__ uint32_t nvfp4_scale_code(float a_b, float s_enc) {
+  const float sf = fminf(div6(a_b) * s_enc, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sf, 0.0f, 0, false) & 0xFFu;
+}
+
+// Encode factor for every E4M3 scale code: enc = s_enc / S (0 for S == 0),
+// clamped to FLT_MAX.  Filled once per workgroup into LDS (128 entries).
+__device__ __forceinline__ float nvfp4_enc_of_code(uint32_t c, float s_enc) {
+  if (c == 0) return 0.0f;
+  return fminf(s_enc / e4m3_decode_mag(c), kFltMax);
+}
+
+// Reference block step (one IEEE division), kept for the generic paths.
 struct BlockScale {
   uint32_t code;
   float enc;
 };
 __device__ __forceinline__ BlockScale nvfp4_block_scale(float a_b, float s_enc) {
-  const float t = a_b / 6.0f;
-  const float sf = t * s_enc;
   BlockScale bs;
-  bs.code = e4m3_rne_mag(sf);
-  const float sfq = e4m3_decode_mag(bs.code);
-  bs.enc = sfq == 0.0f ? 0.0f : fminf(s_enc / sfq, kFltMax);
+  bs.code = nvfp4_scale_code(a_b, s_enc);
+  bs.enc = nvfp4_enc_of_code(bs.code, s_enc);
   return bs;
+}
+
+// ---------------------------------------------------------------- E2M1 (hardware pack)
+// Eight FP32 values -> eight E2M1 codes, RNE, packed low nibble first.  The
+// gfx950 packed convert (scale 1.0) implements exactly the E2M1 RNE rule of
+// e2m1_rne_mag plus the sign bit, on every FP32 input (checked
+// exhaustively); byte k of the result holds elements 2k (low) and 2k+1.
+__device__ __forceinline__ uint32_t fp4x8_rne(const float (&v)[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
 }
 
 // ---------------------------------------------------------------- E8M0 (MX)

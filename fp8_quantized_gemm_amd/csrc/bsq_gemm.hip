@@ -25,16 +25,12 @@
 // sits in which slot, so lane half h takes one contiguous run of the stage
 // (NVFP4: elements [64h, 64h+64), 8 per step over 8 steps; MX: one 32-element
 // block per step) and reads it from LDS with 16-byte loads.
+#include "bsq_gemm_common.hpp"
 #include "bsq_internal.hpp"
 
 namespace bsq {
 
 namespace {
-
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef int intx8 __attribute__((ext_vector_type(8)));
-typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
-typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256, kBN = 256, kThreads = 512;
 
@@ -52,51 +48,6 @@ struct Cfg {
   static constexpr int STEPS = FMT == kNVFP4 ? BK / 16 : BK / 64;      // MFMA K steps per stage
 };
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;     // NaN stays NaN
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// E4M3 byte `sel` of w -> float (exact; OCP E4M3FN on gfx950).
-template <int SEL>
-__device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
-  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
-}
-
-// Block scale S (E4M3 byte SEL of w) as the FP16 pair {S * 2^7, S * 2^7}
-// (exact: S * 2^7 lies in [2^-2, 57344]).
-template <int SEL>
-__device__ __forceinline__ halfx2 nvfp4_scale_pair(uint32_t w) {
-  const float s = e4m3_to_f32<SEL>(w) * 128.0f;
-  return __builtin_bit_cast(halfx2, __builtin_amdgcn_cvt_pkrtz(s, s));
-}
-
-// 8 E2M1 codes (nibble i = element i of one dword) times a block scale, as 8
-// FP16 values v * S * 2^-7 (exact), in the K order [0, 4, 1, 5, 2, 6, 3, 7].
-// E2M1 is a 1-sign / 2-exponent / 1-mantissa float: moving its magnitude bits
-// to FP16 bits 9..11 and its sign to bit 15 gives exactly v * 2^-14 (code 1,
-// 0.5, lands on the FP16 subnormal 0.5 * 2^-14).  Pairing nibbles i and i+4
-// in one dword makes both halves need the same shifts.  The packed FP16
-// multiply by S * 2^7 is exact: v * S has at most 6 significant bits, its
-// lowest bit is >= 2^-10, so v * S * 2^-7 is representable (FP16 denormals
-// are kept).  The MFMA products then carry 2^-14 per operand pair, undone in
-// the epilogue.
-__device__ __forceinline__ halfx8 dequant8(uint32_t w, halfx2 s2) {
-  const uint32_t d0 = ((w << 9) & 0x0E000E00u) | ((w << 12) & 0x80008000u);
-  const uint32_t d1 = ((w << 5) & 0x0E000E00u) | ((w << 8) & 0x80008000u);
-  const uint32_t d2 = ((w << 1) & 0x0E000E00u) | ((w << 4) & 0x80008000u);
-  const uint32_t d3 = ((w >> 3) & 0x0E000E00u) | (w & 0x80008000u);
-  const halfx2 p0 = __builtin_bit_cast(halfx2, d0) * s2;
-  const halfx2 p1 = __builtin_bit_cast(halfx2, d1) * s2;
-  const halfx2 p2 = __builtin_bit_cast(halfx2, d2) * s2;
-  const halfx2 p3 = __builtin_bit_cast(halfx2, d3) * s2;
-  halfx8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
 // Scaled MFMA with the scale byte chosen by the K step (the byte select must be
 // an immediate).
 template <int FMTC>
@@ -108,11 +59,6 @@ __device__ __forceinline__ floatx16 mfma_mx(int step, const intx8& a, const intx
     case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMTC, FMTC, 2, (int)sa, 2, (int)sb);
     default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMTC, FMTC, 3, (int)sa, 3, (int)sb);
   }
-}
-
-__device__ __forceinline__ float nvfp4_s_dec(float amax) {
-  const float s_enc = amax == 0.0f ? 1.0f : fminf(2688.0f / amax, 3.40282346638528859812e+38f);
-  return 1.0f / s_enc;
 }
 
 // Global -> register staging of one stage of one operand (codes + scales).
@@ -260,59 +206,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
     const uint8_t* LSa = lds_sa(buf);
     const uint8_t* LSb = lds_sb(buf);
 
-    if constexpr (FMT == kNVFP4) {
-      // lane half h owns stage elements [64h, 64h + 64): 32 code bytes, 4 scale bytes
-      uint32_t sca[4], scb[2];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        sca[mi] = *reinterpret_cast<const uint32_t*>(LSa + (wm * 128 + mi * 32 + l32) * 8 + 4 * h);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        scb[ni] = *reinterpret_cast<const uint32_t*>(LSb + (wn * 64 + ni * 32 + l32) * 8 + 4 * h);
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {          // 16-byte reads: 4 K-steps each
-        halfx2 ssa[4][2], ssb[2][2];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          ssa[mi][0] = half == 0 ? nvfp4_scale_pair<0>(sca[mi]) : nvfp4_scale_pair<2>(sca[mi]);
-          ssa[mi][1] = half == 0 ? nvfp4_scale_pair<1>(sca[mi]) : nvfp4_scale_pair<3>(sca[mi]);
-        }
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          ssb[ni][0] = half == 0 ? nvfp4_scale_pair<0>(scb[ni]) : nvfp4_scale_pair<2>(scb[ni]);
-          ssb[ni][1] = half == 0 ? nvfp4_scale_pair<1>(scb[ni]) : nvfp4_scale_pair<3>(scb[ni]);
-        }
-        uint4 ca[4], cb[2];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          ca[mi] = *reinterpret_cast<const uint4*>(La + (wm * 128 + mi * 32 + l32) * C::LDR +
-                                                   32 * h + 16 * half);
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          cb[ni] = *reinterpret_cast<const uint4*>(Lb + (wn * 64 + ni * 32 + l32) * C::LDR +
-                                                   32 * h + 16 * half);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          // K step (4*half + s) covers lane elements 8*(4*half+s) .. +7 -> scale byte 2*half + s/2
-          halfx8 fa[4], fb[2];
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            const uint32_t w = s == 0 ? ca[mi].x : s == 1 ? ca[mi].y : s == 2 ? ca[mi].z : ca[mi].w;
-            fa[mi] = dequant8(w, s < 2 ? ssa[mi][0] : ssa[mi][1]);
-          }
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni) {
-            const uint32_t w = s == 0 ? cb[ni].x : s == 1 ? cb[ni].y : s == 2 ? cb[ni].z : cb[ni].w;
-            fb[ni] = dequant8(w, s < 2 ? ssb[ni][0] : ssb[ni][1]);
-          }
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
-        }
-      }
-    } else {
+    {
       // MX operand layouts of v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 = two
       // 32-element MX blocks per instruction; block b's E8M0 scale comes from
       // lane half b):
@@ -374,8 +268,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
 
   // epilogue: alpha * acc -> BF16 (RNE).  Lane holds column m = l32 of D = C^T,
   // rows n = 8*(r/4) + 4*h + r%4 of each 32x32 tile.
-  float alpha = 1.0f;
-  if (FMT == kNVFP4) alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax) * 16384.0f;   // undo 2^-7 per operand
+  const float alpha = 1.0f;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int64_t m = m0 + wm * 128 + mi * 32 + l32;
@@ -443,8 +336,8 @@ hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* 
                        hipStream_t s) {
   switch (fmt) {
     case kNVFP4:
-      return launch_gemm_t<kNVFP4>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax,
-                                   c, ldc, s);
+      return launch_gemm_nvfp4(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax, c,
+                               ldc, s);
     case kMXFP4:
       return launch_gemm_t<kMXFP4>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax,
                                    c, ldc, s);

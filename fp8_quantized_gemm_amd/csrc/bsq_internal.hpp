@@ -38,6 +38,11 @@ hipError_t launch_quant_tile(Fmt fmt, bool sr, bool rht_col, bool two_d, const v
                              uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                              hipStream_t s);
 
+// NVFP4 GEMM (exact FP16 dequant + FP16 MFMA).
+hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                             const float* aa, const uint8_t* bc, const uint8_t* bs,
+                             const float* ba, void* c, int64_t ldc, hipStream_t s);
+
 // C[M, N] = alpha * A . B^T, block-scaled operands, BF16 out.
 hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,

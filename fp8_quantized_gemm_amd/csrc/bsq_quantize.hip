@@ -67,28 +67,36 @@ __device__ __forceinline__ void rht16_pair(float (&y)[8], bool odd, uint32_t sig
   for (int e = 0; e < 8; ++e) y[e] = y[e] * 0.25f;
 }
 
-// Encode 8 scaled values to 8 E2M1 codes packed low-nibble-first.
+// Encode 8 scaled values to 8 E2M1 codes packed low-nibble-first: RNE on the
+// hardware convert, stochastic rounding in software.
 template <bool SR>
 __device__ __forceinline__ uint32_t encode8_fp4(const float (&v)[8], const R16x8& rnd) {
+  if (!SR) return fp4x8_rne(v);
   uint32_t out = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float a = __builtin_fabsf(v[e]);
-    const uint32_t m = SR ? e2m1_sr_mag(a, rnd.get(e)) : e2m1_rne_mag(a);
+    const uint32_t m = e2m1_sr_mag(__builtin_fabsf(v[e]), rnd.get(e));
     out |= (m | e2m1_sign(v[e])) << (4 * e);
   }
   return out;
 }
 
-// Encode 8 scaled values to 8 signed E4M3 bytes.
+// Encode 8 scaled values to 8 signed E4M3 bytes (RNE, saturating at 448):
+// clamp, then the hardware FP32 -> E4M3 convert (RNE on [0, 464)).
 __device__ __forceinline__ uint2 encode8_fp8(const float (&v)[8]) {
-  uint32_t w[2] = {0u, 0u};
+  float c[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t c = e4m3_rne_mag(__builtin_fabsf(v[e])) | ((f2u(v[e]) >> 24) & 0x80u);
-    w[e >> 2] |= c << (8 * (e & 3));
-  }
-  return make_uint2(w[0], w[1]);
+  for (int e = 0; e < 8; ++e) c[e] = fmaxf(fminf(v[e], 448.0f), -448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// LDS table of encode factors enc[S] = s_enc / S for the 128 E4M3 codes.
+__device__ __forceinline__ void fill_enc_table(float* tab, float s_enc) {
+  for (int c = threadIdx.x; c < 128; c += blockDim.x) tab[c] = nvfp4_enc_of_code((uint32_t)c, s_enc);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
@@ -100,6 +108,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
 // Block-level max into one or two global accumulators.
 __device__ __forceinline__ void block_max_atomic(uint32_t m, float* a0, float* a1) {
   __shared__ uint32_t red[16];
+  __syncthreads();                 // a previous call's reads of red[] are done
   m = wave_max_u32(m);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = m;
@@ -204,7 +213,13 @@ __global__ __launch_bounds__(256) void k_quant_flat(const uint4* __restrict__ x,
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const float s_enc = FMT == kNVFP4 ? nvfp4_s_enc(*amax) : 0.0f;
+  __shared__ float enc_tab[128];
+  float s_enc = 0.0f;
+  if (FMT == kNVFP4) {
+    s_enc = nvfp4_s_enc(*amax);
+    fill_enc_table(enc_tab, s_enc);
+    __syncthreads();
+  }
   for (int64_t base = wave * 64 * kUnroll; base < nchunk; base += nwaves * 64 * kUnroll) {
     uint4 v[kUnroll];
 #pragma unroll
@@ -227,9 +242,8 @@ __global__ __launch_bounds__(256) void k_quant_flat(const uint4* __restrict__ x,
       uint32_t scode;
       float mult;
       if (FMT == kNVFP4) {
-        const BlockScale bs = nvfp4_block_scale(a_b, s_enc);
-        scode = bs.code;
-        mult = bs.enc;
+        scode = nvfp4_scale_code(a_b, s_enc);
+        mult = enc_tab[scode];
       } else {
         const int e = mx_exponent(a_b, FMT == kMXFP4 ? 2 : 8);
         scode = (uint32_t)(e + 127);
@@ -274,12 +288,16 @@ __global__ __launch_bounds__(64) void k_quant_tile(
   const int bx = blockIdx.x % gx, by = blockIdx.x / gx;
   const int lane = threadIdx.x;
   const int64_t c0 = ((int64_t)bx * 64 + lane) * 8;
-  if (c0 >= C) return;                       // whole lane groups leave together (C % BLK == 0)
+  __shared__ float enc_row[128], enc_col[128];
   float s_enc_row = 0.0f, s_enc_col = 0.0f;
   if (FMT == kNVFP4) {
     if (do_row) s_enc_row = nvfp4_s_enc(*amax_row);
     if (do_col) s_enc_col = nvfp4_s_enc(*amax_col);
+    fill_enc_table(enc_row, s_enc_row);
+    fill_enc_table(enc_col, s_enc_col);
+    __syncthreads();
   }
+  if (c0 >= C) return;                       // whole lane groups leave together (C % BLK == 0)
   for (int k = 0; k < rbs; ++k) {
     const int64_t r0 = ((int64_t)by * rbs + k) * BLK;
     if (r0 >= R) break;
@@ -298,7 +316,8 @@ __global__ __launch_bounds__(64) void k_quant_tile(
         for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
       }
       m = max(m, dpp_xor1(m));
-      tile = nvfp4_block_scale(u2f(m), do_row ? s_enc_row : s_enc_col);
+      tile.code = nvfp4_scale_code(u2f(m), do_row ? s_enc_row : s_enc_col);
+      tile.enc = do_row ? enc_row[tile.code] : enc_col[tile.code];
     }
 
     if (do_row) {
@@ -319,9 +338,8 @@ __global__ __launch_bounds__(64) void k_quant_tile(
           m = max(m, dpp_xor1(m));
           if (FMT != kNVFP4) m = max(m, dpp_xor2(m));
           if (FMT == kNVFP4) {
-            const BlockScale bs = nvfp4_block_scale(u2f(m), s_enc_row);
-            scode = bs.code;
-            mult = bs.enc;
+            scode = nvfp4_scale_code(u2f(m), s_enc_row);
+            mult = enc_row[scode];
           } else {
             const int e = mx_exponent(u2f(m), EMAX);
             scode = (uint32_t)(e + 127);
@@ -364,9 +382,8 @@ __global__ __launch_bounds__(64) void k_quant_tile(
 #pragma unroll
           for (int i = 0; i < BLK; ++i) m = max(m, absbits(y[i]));
           if (FMT == kNVFP4) {
-            const BlockScale bs = nvfp4_block_scale(u2f(m), s_enc_col);
-            scode = bs.code;
-            mult = bs.enc;
+            scode = nvfp4_scale_code(u2f(m), s_enc_col);
+            mult = enc_col[scode];
           } else {
             const int e = mx_exponent(u2f(m), EMAX);
             scode = (uint32_t)(e + 127);
