@@ -32,28 +32,31 @@ __device__ __forceinline__ halfx2 nvfp4_scale_pair(uint32_t w) {
 }
 
 // 8 E2M1 codes (nibble i = element i of one dword) times a block scale, as 8
-// FP16 values v * S * 2^-7 (exact), in the K order [0, 4, 1, 5, 2, 6, 3, 7].
-// E2M1 is a 1-sign / 2-exponent / 1-mantissa float: moving its magnitude bits
-// to FP16 bits 9..11 and its sign to bit 15 gives exactly v * 2^-14 (code 1,
-// 0.5, lands on the FP16 subnormal 0.5 * 2^-14).  Pairing nibbles i and i+4
-// in one dword makes both halves need the same shifts.  The packed FP16
-// multiply by S * 2^7 is exact: v * S has at most 6 significant bits, its
-// lowest bit is >= 2^-10, so v * S * 2^-7 is representable (FP16 denormals
-// are kept).  The MFMA products then carry 2^-14 per operand pair, undone in
-// the epilogue.  Any fixed K order works as long as both operands use it.
+// FP16 values v * S * 2^-7 (exact), in element order.
+// E2M1 is a 1-sign / 2-exponent / 1-mantissa float, so an FP16 whose high byte
+// is (sign << 7) | (magnitude bits << 1) and whose low byte is 0 equals
+// exactly v * 2^-14 (code 1, 0.5, lands on the FP16 subnormal 0.5 * 2^-14).
+// The high bytes of the even and odd nibbles are built four at a time, then
+// byte permutes pair them with zero low bytes.  The packed FP16 multiply by
+// S * 2^7 is exact: v * S has at most 6 significant bits and its lowest bit is
+// >= 2^-10, so v * S * 2^-7 is representable (FP16 denormals are kept).  The
+// MFMA products carry 2^-14 per operand pair, undone in the epilogue.
 __device__ __forceinline__ halfx8 dequant8(uint32_t w, halfx2 s2) {
-  const uint32_t d0 = ((w << 9) & 0x0E000E00u) | ((w << 12) & 0x80008000u);
-  const uint32_t d1 = ((w << 5) & 0x0E000E00u) | ((w << 8) & 0x80008000u);
-  const uint32_t d2 = ((w << 1) & 0x0E000E00u) | ((w << 4) & 0x80008000u);
-  const uint32_t d3 = ((w >> 3) & 0x0E000E00u) | (w & 0x80008000u);
+  const uint32_t he = ((w & 0x07070707u) << 1) | ((w << 4) & 0x80808080u);          // nibbles 0,2,4,6
+  const uint32_t ho = (((w >> 4) & 0x07070707u) << 1) | (w & 0x80808080u);          // nibbles 1,3,5,7
+  // dword k = FP16 {element 2k, element 2k+1}: bytes {0, he.k, 0, ho.k}
+  const uint32_t d0 = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
+  const uint32_t d1 = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
+  const uint32_t d2 = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
+  const uint32_t d3 = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
   const halfx2 p0 = __builtin_bit_cast(halfx2, d0) * s2;
   const halfx2 p1 = __builtin_bit_cast(halfx2, d1) * s2;
   const halfx2 p2 = __builtin_bit_cast(halfx2, d2) * s2;
   const halfx2 p3 = __builtin_bit_cast(halfx2, d3) * s2;
-  halfx8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+  return __builtin_bit_cast(halfx8, make_uint4(__builtin_bit_cast(uint32_t, p0),
+                                               __builtin_bit_cast(uint32_t, p1),
+                                               __builtin_bit_cast(uint32_t, p2),
+                                               __builtin_bit_cast(uint32_t, p3)));
 }
 
 __device__ __forceinline__ float nvfp4_s_dec(float amax) {

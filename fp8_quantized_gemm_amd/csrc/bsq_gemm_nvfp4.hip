@@ -43,12 +43,20 @@ struct NvChunk {
   uint32_t scales;          // block scale bytes in bits 0..7 and 8..15
 };
 
+// FP16 scale pairs of a chunk's two blocks.
+struct NvScales {
+  halfx2 s0, s1;
+};
+__device__ __forceinline__ NvScales nv_scales(const NvChunk& c) {
+  return NvScales{nvfp4_scale_pair<0>(c.scales), nvfp4_scale_pair<1>(c.scales)};
+}
+
 // Chunk of thread t for stage kt: row t/2 of the 256-row tile, half t%2 of
 // the stage's 64 elements.  Rows past the end re-read the last row (their
 // results are never stored).  FAST: whole chunks in bounds and aligned.
 template <bool FAST>
-__device__ __forceinline__ void nv_load(NvChunk& c, const uint8_t* __restrict__ codes,
-                                        const uint8_t* __restrict__ scales, int64_t rows,
+__device__ __forceinline__ void nv_load(NvChunk& c, const uint8_t* codes,
+                                        const uint8_t* scales, int64_t rows,
                                         int64_t row0, int64_t kt, int64_t code_ld,
                                         int64_t scale_ld) {
   const int t = threadIdx.x;
@@ -72,27 +80,98 @@ __device__ __forceinline__ void nv_load(NvChunk& c, const uint8_t* __restrict__ 
   }
 }
 
-// Expand group g (8 elements) of a chunk to FP16 and store it to the LDS tile.
+// Expand group G (8 elements) of a chunk to FP16 and store it to the LDS tile.
 template <int G>
-__device__ __forceinline__ void nv_store_group(const NvChunk& c, uint8_t* lds_op) {
+__device__ __forceinline__ void nv_store_group(const NvChunk& c, const NvScales& sc,
+                                               uint8_t* lds_op) {
   const int t = threadIdx.x;
   const uint32_t w = G == 0 ? c.codes.x : G == 1 ? c.codes.y : G == 2 ? c.codes.z : c.codes.w;
-  const halfx2 s2 = G < 2 ? nvfp4_scale_pair<0>(c.scales) : nvfp4_scale_pair<1>(c.scales);
-  *reinterpret_cast<halfx8*>(lds_op + (t >> 1) * kNvRowB + (t & 1) * 64 + G * 16) = dequant8(w, s2);
+  *reinterpret_cast<halfx8*>(lds_op + (t >> 1) * kNvRowB + (t & 1) * 64 + G * 16) =
+      dequant8(w, G < 2 ? sc.s0 : sc.s1);
 }
 
 template <int G>
-__device__ __forceinline__ void nv_store_group2(const NvChunk& a, const NvChunk& b, uint8_t* la,
-                                                uint8_t* lb) {
-  nv_store_group<G>(a, la);
-  nv_store_group<G>(b, lb);
+__device__ __forceinline__ void nv_store_group2(const NvChunk& a, const NvScales& sa,
+                                                const NvChunk& b, const NvScales& sb,
+                                                uint8_t* la, uint8_t* lb) {
+  nv_store_group<G>(a, sa, la);
+  nv_store_group<G>(b, sb, lb);
+}
+
+// Fragments of one 16-wide K step: 4 A tiles and 2 B tiles of 32 rows.
+struct NvFrags {
+  halfx8 a[4], b[2];
+};
+__device__ __forceinline__ void nv_frags(NvFrags& f, const uint8_t* La, const uint8_t* Lb, int s,
+                                         int wm, int wn, int h, int l32) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+    f.a[mi] = *reinterpret_cast<const halfx8*>(La + (wm * 128 + mi * 32 + l32) * kNvRowB + s * 32 + h * 16);
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+    f.b[ni] = *reinterpret_cast<const halfx8*>(Lb + (wn * 64 + ni * 32 + l32) * kNvRowB + s * 32 + h * 16);
+}
+
+// One K stage, straight-line: MFMAs on LDS buffer `buf` (stage kt) while the
+// chunks of stage kt+1 (ca, cb) are expanded into the other buffer and the
+// loads of stage kt+2 go into (na, nb).  Fragments of the next 16-wide K step
+// are read while the current step's MFMAs run; scheduling groups interleave
+// MFMA, LDS and VALU work.  At the last stages the prefetch re-reads the last
+// stage and the expansion writes an unused buffer (never read before the
+// final barrier), which keeps the code branch-free.
+template <bool FAST>
+__device__ __forceinline__ void nv_stage(floatx16 (&acc)[4][2], uint8_t* smem, int64_t kt,
+                                         int64_t KT, const NvChunk& ca, const NvChunk& cb,
+                                         NvChunk& na, NvChunk& nb, const uint8_t* a_codes,
+                                         const uint8_t* a_scales, const uint8_t* b_codes,
+                                         const uint8_t* b_scales, int64_t M, int64_t N,
+                                         int64_t m0, int64_t n0, int64_t code_ld,
+                                         int64_t scale_ld, int wm, int wn, int h, int l32) {
+  const int buf = (int)(kt & 1);
+  const int64_t kp = kt + 2 < KT ? kt + 2 : KT - 1;
+  nv_load<FAST>(na, a_codes, a_scales, M, m0, kp, code_ld, scale_ld);
+  nv_load<FAST>(nb, b_codes, b_scales, N, n0, kp, code_ld, scale_ld);
+  // keep the prefetch here (the operand pointers are deliberately not
+  // __restrict__, so these loads cannot be sunk towards their use in the next
+  // stage, where they would then have to be waited for)
+  asm volatile("" ::: "memory");
+  const uint8_t* La = smem + buf * kNvStageB;
+  const uint8_t* Lb = La + kNvOpB;
+  uint8_t* Na = smem + (buf ^ 1) * kNvStageB;
+  uint8_t* Nb = Na + kNvOpB;
+  const NvScales sa = nv_scales(ca), sb = nv_scales(cb);
+  NvFrags f[2];
+  nv_frags(f[0], La, Lb, 0, wm, wn, h, l32);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    NvFrags& cur = f[s & 1];
+    if (s < 3) nv_frags(f[(s + 1) & 1], La, Lb, s + 1, wm, wn, h, l32);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[ni], cur.a[mi], acc[mi][ni], 0, 0, 0);
+    if (s == 0) nv_store_group2<0>(ca, sa, cb, sb, Na, Nb);
+    if (s == 1) nv_store_group2<1>(ca, sa, cb, sb, Na, Nb);
+    if (s == 2) nv_store_group2<2>(ca, sa, cb, sb, Na, Nb);
+    if (s == 3) nv_store_group2<3>(ca, sa, cb, sb, Na, Nb);
+    // 8 MFMAs, each followed by one fragment read (6) and ~4 VALU ops of the
+    // expansion; the two LDS writes of the expanded group last.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+      if (s < 3 && i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);              // VALU
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);                // DS write
+  }
+  __syncthreads();
 }
 
 template <bool FAST>
 __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4(
-    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes,
-    const uint8_t* __restrict__ a_scales, const float* __restrict__ a_amax,
-    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
+    int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+    const float* __restrict__ a_amax, const uint8_t* b_codes, const uint8_t* b_scales,
     const float* __restrict__ b_amax, uint16_t* __restrict__ c, int64_t ldc, int tiles_m,
     int tiles_n, int vec_store) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -113,58 +192,29 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  NvChunk a1{}, b1{};
+  NvChunk xa, xb, ya, yb;                          // two register sets, used alternately
   if (KT > 0) {
     NvChunk a0, b0;
     nv_load<FAST>(a0, a_codes, a_scales, M, m0, 0, code_ld, scale_ld);
     nv_load<FAST>(b0, b_codes, b_scales, N, n0, 0, code_ld, scale_ld);
-    nv_store_group2<0>(a0, b0, smem, smem + kNvOpB);
-    nv_store_group2<1>(a0, b0, smem, smem + kNvOpB);
-    nv_store_group2<2>(a0, b0, smem, smem + kNvOpB);
-    nv_store_group2<3>(a0, b0, smem, smem + kNvOpB);
+    const NvScales sa = nv_scales(a0), sb = nv_scales(b0);
+    nv_store_group2<0>(a0, sa, b0, sb, smem, smem + kNvOpB);
+    nv_store_group2<1>(a0, sa, b0, sb, smem, smem + kNvOpB);
+    nv_store_group2<2>(a0, sa, b0, sb, smem, smem + kNvOpB);
+    nv_store_group2<3>(a0, sa, b0, sb, smem, smem + kNvOpB);
   }
   if (KT > 1) {
-    nv_load<FAST>(a1, a_codes, a_scales, M, m0, 1, code_ld, scale_ld);
-    nv_load<FAST>(b1, b_codes, b_scales, N, n0, 1, code_ld, scale_ld);
+    nv_load<FAST>(xa, a_codes, a_scales, M, m0, 1, code_ld, scale_ld);
+    nv_load<FAST>(xb, b_codes, b_scales, N, n0, 1, code_ld, scale_ld);
   }
   __syncthreads();
 
-  for (int64_t kt = 0; kt < KT; ++kt) {
-    const int buf = (int)(kt & 1);
-    const bool has1 = kt + 1 < KT, has2 = kt + 2 < KT;
-    NvChunk a2{}, b2{};
-    if (has2) {
-      nv_load<FAST>(a2, a_codes, a_scales, M, m0, kt + 2, code_ld, scale_ld);
-      nv_load<FAST>(b2, b_codes, b_scales, N, n0, kt + 2, code_ld, scale_ld);
-    }
-    const uint8_t* La = smem + buf * kNvStageB;
-    const uint8_t* Lb = La + kNvOpB;
-    uint8_t* Na = smem + (buf ^ 1) * kNvStageB;
-    uint8_t* Nb = Na + kNvOpB;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      halfx8 fa[4], fb[2];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        fa[mi] = *reinterpret_cast<const halfx8*>(La + (wm * 128 + mi * 32 + l32) * kNvRowB + s * 32 + h * 16);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        fb[ni] = *reinterpret_cast<const halfx8*>(Lb + (wn * 64 + ni * 32 + l32) * kNvRowB + s * 32 + h * 16);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
-      if (has1) {
-        if (s == 0) nv_store_group2<0>(a1, b1, Na, Nb);
-        if (s == 1) nv_store_group2<1>(a1, b1, Na, Nb);
-        if (s == 2) nv_store_group2<2>(a1, b1, Na, Nb);
-        if (s == 3) nv_store_group2<3>(a1, b1, Na, Nb);
-      }
-    }
-    __syncthreads();
-    a1 = a2;
-    b1 = b2;
+  for (int64_t kt = 0; kt < KT; kt += 2) {
+    nv_stage<FAST>(acc, smem, kt, KT, xa, xb, ya, yb, a_codes, a_scales, b_codes, b_scales, M, N,
+                   m0, n0, code_ld, scale_ld, wm, wn, h, l32);
+    if (kt + 1 < KT)
+      nv_stage<FAST>(acc, smem, kt + 1, KT, ya, yb, xa, xb, a_codes, a_scales, b_codes, b_scales,
+                     M, N, m0, n0, code_ld, scale_ld, wm, wn, h, l32);
   }
 
   // ---- epilogue: alpha * acc -> BF16, staged per wave through LDS.
