@@ -24,25 +24,42 @@ import numpy as np
 
 
 def rht16(chunks, signs):
-    """chunks: float32 array [..., 16]; signs: int 0..65535.  Returns float32 [..., 16]."""
+    """chunks: float32 array [..., 16]; signs: int 0..65535.  Returns float32 [..., 16].
+
+    Stage h pairs element i (with i & h == 0) with element i + h; viewing the
+    last axis as [16 / (2h), 2, h] puts such pairs at [..., k, 0, j] and
+    [..., k, 1, j], so each stage is one float32 add and one subtract over the
+    whole array, in the same pairs and order as the scalar butterfly."""
     y = np.array(chunks, dtype=np.float32, copy=True)
     assert y.shape[-1] == 16
     signs = int(signs) & 0xFFFF
-    for i in range(16):
-        if (signs >> i) & 1:
-            y[..., i] = -y[..., i]
+    d = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)], dtype=np.float32)
+    y *= d                                   # exact sign flips (multiplication by +-1)
+    lead = y.shape[:-1]
     h = 1
     while h < 16:
-        out = y.copy()
-        for i in range(16):
-            if i & h == 0:
-                a = y[..., i]
-                b = y[..., i + h]
-                out[..., i] = a + b          # float32 add, RNE
-                out[..., i + h] = a - b
-        y = out
+        v = y.reshape(lead + (16 // (2 * h), 2, h))
+        a = v[..., 0, :]
+        b = v[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2).reshape(lead + (16,))
         h *= 2
     return (y * np.float32(0.25)).astype(np.float32)
+
+
+def rht16_scalar(chunk, signs):
+    """The same transform on one 16-element chunk, element by element (for pins)."""
+    y = [np.float32(v) for v in chunk]
+    for i in range(16):
+        if (int(signs) >> i) & 1:
+            y[i] = -y[i]
+    h = 1
+    while h < 16:
+        for i in range(16):
+            if i & h == 0:
+                a, b = y[i], y[i + h]
+                y[i], y[i + h] = np.float32(a + b), np.float32(a - b)
+        h *= 2
+    return np.array([np.float32(v * np.float32(0.25)) for v in y], dtype=np.float32)
 
 
 def rht_matrix_f64(signs):

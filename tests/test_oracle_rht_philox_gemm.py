@@ -230,3 +230,12 @@ def test_tolerance_rule_accepts_bf16_rounding_and_rejects_planted_mistakes():
     assert not G.tolerance_report(bad, C)["passed"]
     # a dropped per-tensor scale
     assert not G.tolerance_report(C / G.nvfp4_alpha(aa, ba) * 1.01 * G.nvfp4_alpha(aa, ba) * 1.03, C)["passed"]
+
+
+def test_rht_vectorized_equals_scalar_butterfly():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((40, 16)) * 10.0 ** rng.uniform(-3, 3, (40, 1))).astype(np.float32)
+    for signs in (0, 0x8421, 0xFFFF):
+        v = R.rht16(x, signs)
+        for r in range(40):
+            assert np.array_equal(v[r], R.rht16_scalar(x[r], signs))
