@@ -131,6 +131,23 @@ class Step:
         timed("WGRAD_gu", lambda: self.gemm(G["WGRAD_gu"]))
 
 
+def gemm_traffic(workload):
+    """HBM bytes per k_gemm_nvfp4 launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload, or None when the kernel sources have
+    changed since those counters were taken (the summary stores their SHA-256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"nvfp4_gemm_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def cpu_baseline(workload, rht):
     """The oracle on a bounded slice of the same workload: FPROP_gu for the first
     TOK tokens and the first NOUT output features (quantize X rows 1x16 RNE,
@@ -236,7 +253,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "bsq k_gemm<NVFP4> (6 launches per step)",
                      "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": gemm_traffic(args.workload),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)"},
         "breakdown": breakdown,
         "wall_s": round(wall, 3),
     }
