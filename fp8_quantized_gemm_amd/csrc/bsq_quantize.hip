@@ -67,18 +67,11 @@ __device__ __forceinline__ void rht16_pair(float (&y)[8], bool odd, uint32_t sig
   for (int e = 0; e < 8; ++e) y[e] = y[e] * 0.25f;
 }
 
-// Encode 8 scaled values to 8 E2M1 codes packed low-nibble-first: RNE on the
-// hardware convert, stochastic rounding in software.
+// Encode 8 scaled values to 8 E2M1 codes packed low-nibble-first: RNE or
+// stochastic rounding, both on the hardware converts.
 template <bool SR>
 __device__ __forceinline__ uint32_t encode8_fp4(const float (&v)[8], const R16x8& rnd) {
-  if (!SR) return fp4x8_rne(v);
-  uint32_t out = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t m = e2m1_sr_mag(__builtin_fabsf(v[e]), rnd.get(e));
-    out |= (m | e2m1_sign(v[e])) << (4 * e);
-  }
-  return out;
+  return SR ? fp4x8_sr(v, rnd) : fp4x8_rne(v);
 }
 
 // Encode 8 scaled values to 8 signed E4M3 bytes (RNE, saturating at 448):
@@ -411,6 +404,169 @@ __global__ __launch_bounds__(64) void k_quant_tile(
   }
 }
 
+// ---------------------------------------------------------------- NVFP4 row + column encoder, 256 x 256 tiles
+//
+// One 512-thread workgroup per 256 x 256 tile (R and C multiples of 256).
+// Thread t owns columns 8 * (t % 32) .. +8 of the tile and its 16-row block
+// t / 32, so every 1x16 column block (and every 16x16 weight tile, with the
+// neighbouring lane) sits in registers, exactly as in k_quant_tile.  What
+// differs is the output path: row codes go straight out (32 lanes write one
+// 128-byte row segment), while column codes and both scale arrays are staged in
+// LDS and written as whole 128-byte lines (column codes) or 16-byte runs
+// (scales), so no partial line is left for the L2 to merge.  Tiles are dealt
+// to the XCDs in contiguous runs of the row-major tile order, so the eight
+// tiles that share a row-scale line finish in one L2.
+constexpr int kQtThreads = 512;
+constexpr int kQtTile = 256;
+
+__device__ __forceinline__ void qt_tile_of_block(int pid, int tiles_r, int tiles_c, int& tr, int& tc) {
+  constexpr int kXcd = 8;
+  const int nt = tiles_r * tiles_c;
+  const int q = nt / kXcd, r = nt % kXcd;
+  const int xcd = pid % kXcd, i = pid / kXcd;
+  const int idx = xcd * q + (xcd < r ? xcd : r) + i;
+  tr = idx / tiles_c;
+  tc = idx % tiles_c;
+}
+
+template <bool SR, bool RHT, bool TWO_D>
+__global__ __launch_bounds__(kQtThreads) void k_qt_nvfp4(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int tiles_r, int tiles_c, int do_row,
+    int do_col, const float* __restrict__ amax_row, const float* __restrict__ amax_col,
+    uint32_t signs, uint64_t seed, uint32_t offset, uint8_t* __restrict__ codes_row,
+    uint8_t* __restrict__ scales_row, uint8_t* __restrict__ codes_col,
+    uint8_t* __restrict__ scales_col) {
+  // column codes: 256 columns x 128 bytes, 8-byte unit u of column c stored at
+  // unit u ^ ((c / 8) % 16), so the 16 lanes of a write phase hit distinct banks
+  __shared__ __attribute__((aligned(16))) uint8_t col_codes[kQtTile * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t col_sc[16 * kQtTile];   // [row block][column]
+  __shared__ __attribute__((aligned(16))) uint8_t row_sc[kQtTile * 16];   // [row][column block]
+  __shared__ float enc_row[128], enc_col[128];
+  int tr, tc;
+  qt_tile_of_block(blockIdx.x, tiles_r, tiles_c, tr, tc);
+  const int t = threadIdx.x, cg = t & 31, rb = t >> 5;
+  const int64_t r0 = (int64_t)tr * kQtTile + rb * 16, c0 = (int64_t)tc * kQtTile + cg * 8;
+
+  uint4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * C + c0);
+
+  const float s_enc_row = do_row ? nvfp4_s_enc(*amax_row) : 0.0f;
+  const float s_enc_col = do_col ? nvfp4_s_enc(*amax_col) : 0.0f;
+  if (t < 128) enc_row[t] = nvfp4_enc_of_code((uint32_t)t, s_enc_row);
+  else if (t < 256) enc_col[t - 128] = nvfp4_enc_of_code((uint32_t)(t - 128), s_enc_col);
+  __syncthreads();
+
+  BlockScale tile{};
+  if (TWO_D) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float y[8];
+      unpack8(v[i], y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
+    }
+    m = max(m, dpp_xor1(m));
+    tile.code = nvfp4_scale_code(u2f(m), do_row ? s_enc_row : s_enc_col);
+    tile.enc = do_row ? enc_row[tile.code] : enc_col[tile.code];
+  }
+
+  if (do_row) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float y[8];
+      unpack8(v[i], y);
+      uint32_t scode;
+      float mult;
+      if (TWO_D) {
+        scode = tile.code;
+        mult = tile.enc;
+      } else {
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
+        m = max(m, dpp_xor1(m));
+        scode = nvfp4_scale_code(u2f(m), s_enc_row);
+        mult = enc_row[scode];
+      }
+      float v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v8[e] = y[e] * mult;
+      const int64_t flat = (r0 + i) * C + c0;
+      R16x8 rnd{};
+      if (SR) rnd = sr_words((uint64_t)(flat >> 3), seed, offset, 0u);
+      reinterpret_cast<uint32_t*>(codes_row)[flat >> 3] = encode8_fp4<SR>(v8, rnd);
+      if ((cg & 1) == 0) row_sc[(rb * 16 + i) * 16 + (cg >> 1)] = (uint8_t)scode;
+    }
+  }
+
+  if (do_col) {
+    uint32_t sc_lo = 0, sc_hi = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = tile_elem(v[i], j);
+      if (RHT) rht16(y, signs);
+      uint32_t scode;
+      float mult;
+      if (TWO_D) {
+        scode = tile.code;
+        mult = tile.enc;
+      } else {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = max(m, absbits(y[i]));
+        scode = nvfp4_scale_code(u2f(m), s_enc_col);
+        mult = enc_col[scode];
+      }
+      const int64_t flat = (c0 + j) * R + r0;
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = y[8 * h + e] * mult;
+        R16x8 rnd{};
+        if (SR) rnd = sr_words((uint64_t)(flat >> 3) + h, seed, offset, 1u);
+        w[h] = encode8_fp4<SR>(v8, rnd);
+      }
+      const int cl = cg * 8 + j;
+      *reinterpret_cast<uint2*>(col_codes + cl * 128 + ((rb ^ (cg & 15)) << 3)) = make_uint2(w[0], w[1]);
+      if (j < 4) sc_lo |= scode << (8 * j);
+      else sc_hi |= scode << (8 * (j - 4));
+    }
+    *reinterpret_cast<uint2*>(col_sc + rb * kQtTile + cg * 8) = make_uint2(sc_lo, sc_hi);
+  }
+  __syncthreads();
+
+  if (do_col) {
+    const int64_t ld = R / 2;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = t + kQtThreads * k;
+      const int cl = q >> 3, ch = q & 7;
+      const int f = (cl >> 3) & 15;
+      uint4 val = *reinterpret_cast<const uint4*>(col_codes + cl * 128 + (((2 * ch) ^ (f & 14)) << 3));
+      if (f & 1) val = make_uint4(val.z, val.w, val.x, val.y);
+      *reinterpret_cast<uint4*>(codes_col + ((int64_t)tc * kQtTile + cl) * ld + (int64_t)tr * 128 + ch * 16) = val;
+    }
+    if (t < kQtTile) {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int b = 0; b < 16; ++b) w[b >> 2] |= (uint32_t)col_sc[b * kQtTile + t] << (8 * (b & 3));
+      *reinterpret_cast<uint4*>(scales_col + ((int64_t)tc * kQtTile + t) * (R / 16) + (int64_t)tr * 16) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  if (do_row && t >= kQtThreads - kQtTile) {
+    const int row = t - (kQtThreads - kQtTile);
+    *reinterpret_cast<uint4*>(scales_row + ((int64_t)tr * kQtTile + row) * (C / 16) + (int64_t)tc * 16) =
+        *reinterpret_cast<const uint4*>(row_sc + row * 16);
+  }
+}
+
 // Row-blocks per lane: as many as keeps >= 4096 waves in flight (up to 16).
 int pick_rbs(int64_t nrowblocks, int64_t waves_x) {
   int rbs = 16;
@@ -491,6 +647,25 @@ hipError_t launch_quant_tile(Fmt fmt, bool sr, bool rht_col, bool two_d, const v
                              uint64_t seed, uint32_t offset, uint8_t* codes_row,
                              uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                              hipStream_t s) {
+  const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (fmt == kNVFP4 && R % kQtTile == 0 && C % kQtTile == 0 && R > 0 && C > 0 && al16(x) &&
+      (!do_row || (al16(codes_row) && al16(scales_row))) &&
+      (!do_col || (al16(codes_col) && al16(scales_col))) &&
+      (R / kQtTile) * (C / kQtTile) < (int64_t)1 << 31) {
+    const int tiles_r = (int)(R / kQtTile), tiles_c = (int)(C / kQtTile);
+    const dim3 grid((unsigned)(tiles_r * tiles_c)), block(kQtThreads);
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    const int dr = do_row ? 1 : 0, dc = do_col ? 1 : 0;
+#define BSQ_QT(S, H, D)                                                                           \
+  hipLaunchKernelGGL((k_qt_nvfp4<S, H, D>), grid, block, 0, s, xp, R, C, tiles_r, tiles_c, dr, dc, \
+                     amax_row, amax_col, signs, seed, offset, codes_row, scales_row, codes_col,   \
+                     scales_col)
+    if (two_d) BSQ_QT(false, false, true);
+    else if (sr) { if (rht_col) BSQ_QT(true, true, false); else BSQ_QT(true, false, false); }
+    else { if (rht_col) BSQ_QT(false, true, false); else BSQ_QT(false, false, false); }
+#undef BSQ_QT
+    return hipGetLastError();
+  }
   const int blk = fmt == kNVFP4 ? 16 : 32;
   const int64_t lanes = C / 8;
   const int gx = (int)((lanes + 63) / 64);

@@ -96,10 +96,12 @@ def test_quantize_transpose(shape, case):
         assert_bytes_equal(u8(out[k + "_codes"]), ref[k + "_codes"], k + " codes")
 
 
+# (512, 256) runs the 256 x 256 tiled kernel, (128, 64) the general one.
+@pytest.mark.parametrize("shape", [(128, 64), (512, 256)])
 @pytest.mark.parametrize("row,col", [(True, False), (False, True)])
-def test_quantize_transpose_one_orientation(row, col):
-    announce("quantize_transpose one side", row, col)
-    x = synth.bf16_tensor((128, 64), 21, device="cuda")
+def test_quantize_transpose_one_orientation(row, col, shape):
+    announce("quantize_transpose one side", row, col, shape)
+    x = synth.bf16_tensor(shape, 21, device="cuda")
     out = bsq.quantize_transpose(x, "nvfp4", 1, "sr", 3, 0, rht_col=True, rht_signs=0x1234,
                                  row=row, col=col)
     torch.cuda.synchronize()
@@ -127,10 +129,11 @@ def _special_bits(R, C, seed):
     return b
 
 
+@pytest.mark.parametrize("shape", [(32, 64), (256, 256)])
 @pytest.mark.parametrize("rnd", ["rne", "sr"])
-def test_special_values_nvfp4(rnd):
-    announce("special values nvfp4", rnd)
-    b = _special_bits(32, 64, 1)
+def test_special_values_nvfp4(rnd, shape):
+    announce("special values nvfp4", rnd, shape)
+    b = _special_bits(*shape, 1)
     x = from_bits(b)
     out = bsq.quantize_transpose(x, "nvfp4", 1, rnd, 5, 0, rht_col=True, rht_signs=0xFFFF)
     c, s, a = bsq.nvfp4_quantize(x, 1, rnd, 5, 0)
