@@ -129,29 +129,32 @@ __global__ void k_copy_amax(const float* src, float* dst) {
 
 // ---------------------------------------------------------------- amax passes
 
+constexpr int kAmaxPer = 8;         // chunks per thread per trip (amax pass)
+
+// Grid-stride amax: each trip a thread loads kAmaxPer 16-byte chunks (a wave
+// reads kAmaxPer runs of 1 KiB) before reducing them; at most 2048 workgroups,
+// so the closing per-workgroup atomics stay few.
 template <bool RHT>
 __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, int64_t nchunk,
                                                    uint32_t signs, float* a0, float* a1) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int t = threadIdx.x, lane = t & 63;
   uint32_t m = 0;
-  for (int64_t base = wave * 64 * kUnroll; base < nchunk; base += nwaves * 64 * kUnroll) {
-    uint4 v[kUnroll];
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kAmaxPer; base < nchunk;
+       base += (int64_t)gridDim.x * 256 * kAmaxPer) {
+    uint4 v[kAmaxPer];
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t q = base + k * 64 + lane;
+    for (int k = 0; k < kAmaxPer; ++k) {
+      const int64_t q = base + k * 256 + t;
       v[k] = q < nchunk ? x[q] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
+    for (int k = 0; k < kAmaxPer; ++k) {
       if (!RHT) {
+        // BF16 magnitudes compare as unsigned 15-bit integers; the widening to
+        // FP32 bits (<< 16) keeps the order
         const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          m = max(m, (w[i] & 0x7FFFu) << 16);
-          m = max(m, w[i] & 0x7FFF0000u);
-        }
+        for (int i = 0; i < 4; ++i) m = max(m, max((w[i] & 0x7FFFu) << 16, w[i] & 0x7FFF0000u));
       } else {
         float y[8];
         unpack8(v[k], y);
@@ -597,7 +600,9 @@ hipError_t launch_copy_amax(const float* src, float* dst, hipStream_t s) {
 
 hipError_t launch_amax_flat(const void* x, int64_t nchunk, bool rht, uint32_t signs, float* a0,
                             float* a1, hipStream_t s) {
-  const dim3 grid((unsigned)flat_grid(nchunk)), block(256);
+  int64_t g = (nchunk + 256 * kAmaxPer - 1) / (256 * kAmaxPer);
+  g = g < 1 ? 1 : (g > 2048 ? 2048 : g);
+  const dim3 grid((unsigned)g), block(256);
   const uint4* xp = static_cast<const uint4*>(x);
   if (rht)
     hipLaunchKernelGGL(k_amax_flat<true>, grid, block, 0, s, xp, nchunk, signs, a0, a1);
