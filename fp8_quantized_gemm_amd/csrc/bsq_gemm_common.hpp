@@ -33,26 +33,20 @@ __device__ __forceinline__ halfx2 nvfp4_scale_pair(uint32_t w) {
 
 // 8 E2M1 codes (nibble i = element i of one dword) times a block scale, as 8
 // FP16 values v * S * 2^-7 (exact), in element order.
-// E2M1 is a 1-sign / 2-exponent / 1-mantissa float, so an FP16 whose high byte
-// is (sign << 7) | (magnitude bits << 1) and whose low byte is 0 equals
-// exactly v * 2^-14 (code 1, 0.5, lands on the FP16 subnormal 0.5 * 2^-14).
-// The high bytes of the even and odd nibbles are built four at a time, then
-// byte permutes pair them with zero low bytes.  The packed FP16 multiply by
-// S * 2^7 is exact: v * S has at most 6 significant bits and its lowest bit is
-// >= 2^-10, so v * S * 2^-7 is representable (FP16 denormals are kept).  The
-// MFMA products carry 2^-14 per operand pair, undone in the epilogue.
+// gfx950's FP4 -> FP16 pair convert turns byte k of the dword (elements 2k and
+// 2k + 1, low nibble first) into two FP16 values multiplied by the power of
+// two of its scale operand; with 2^-14 it yields v * 2^-14 exactly, FP16
+// subnormals and signed zeros included (checked on every byte value at scales
+// 1, 2^-7, 2^-14 and 2^-20).  The packed FP16 multiply by S * 2^7 is exact:
+// v * S has at most 6 significant bits and its lowest bit is >= 2^-10, so
+// v * S * 2^-7 is representable (FP16 denormals are kept).  The MFMA products
+// carry 2^-14 per operand pair, undone in the epilogue.
 __device__ __forceinline__ halfx8 dequant8(uint32_t w, halfx2 s2) {
-  const uint32_t he = ((w & 0x07070707u) << 1) | ((w << 4) & 0x80808080u);          // nibbles 0,2,4,6
-  const uint32_t ho = (((w >> 4) & 0x07070707u) << 1) | (w & 0x80808080u);          // nibbles 1,3,5,7
-  // dword k = FP16 {element 2k, element 2k+1}: bytes {0, he.k, 0, ho.k}
-  const uint32_t d0 = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
-  const uint32_t d1 = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
-  const uint32_t d2 = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
-  const uint32_t d3 = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
-  const halfx2 p0 = __builtin_bit_cast(halfx2, d0) * s2;
-  const halfx2 p1 = __builtin_bit_cast(halfx2, d1) * s2;
-  const halfx2 p2 = __builtin_bit_cast(halfx2, d2) * s2;
-  const halfx2 p3 = __builtin_bit_cast(halfx2, d3) * s2;
+  const float k = 0x1p-14f;
+  const halfx2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, k, 0) * s2;
+  const halfx2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, k, 1) * s2;
+  const halfx2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, k, 2) * s2;
+  const halfx2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, k, 3) * s2;
   return __builtin_bit_cast(halfx8, make_uint4(__builtin_bit_cast(uint32_t, p0),
                                                __builtin_bit_cast(uint32_t, p1),
                                                __builtin_bit_cast(uint32_t, p2),

@@ -51,6 +51,50 @@ __device__ __forceinline__ NvScales nv_scales(const NvChunk& c) {
   return NvScales{nvfp4_scale_pair<0>(c.scales), nvfp4_scale_pair<1>(c.scales)};
 }
 
+// Epilogue shared by both kernels: alpha * acc -> BF16, staged per wave through
+// LDS so that global stores are whole 128-byte row segments.  Lane holds output
+// row m = 32 mi + l32 and columns n = 32 ni + 8 q + 4 h + e (e = 0..3) of the
+// wave's 128 x 64 tile (D = B_tile . A_tile^T layout).  The caller has passed a
+// barrier after the last LDS read of the main loop.
+__device__ __forceinline__ void nv_epilogue(const floatx16 (&acc)[4][2], uint8_t* smem,
+                                            const float* a_amax, const float* b_amax, uint16_t* c,
+                                            int64_t ldc, int64_t M, int64_t N, int64_t m0,
+                                            int64_t n0, int wm, int wn, int lane, int vec_store) {
+  const int h = lane >> 5, l32 = lane & 31, wave = threadIdx.x >> 6;
+  const float alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax) * 16384.0f;   // undo 2^-7 per operand
+  uint8_t* E = smem + wave * (128 * kNvEpiRowB);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(acc[mi][ni][4 * q + e] * alpha);
+        *reinterpret_cast<uint2*>(E + (mi * 32 + l32) * kNvEpiRowB + (ni * 32 + q * 8 + h * 4) * 2) =
+            make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      }
+  __syncthreads();
+  const int64_t gm0 = m0 + wm * 128, gn = n0 + wn * 64 + (lane & 7) * 8;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 8 + (lane >> 3);
+    const int64_t gm = gm0 + row;
+    if (gm >= M) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(E + row * kNvEpiRowB + (lane & 7) * 16);
+    uint16_t* dst = c + gm * ldc + gn;
+    if (vec_store && gn + 7 < N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gn + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
 // Chunk of thread t for stage kt: row t/2 of the 256-row tile, half t%2 of
 // the stage's 64 elements.  Rows past the end re-read the last row (their
 // results are never stored).  FAST: whole chunks in bounds and aligned.
@@ -217,41 +261,269 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4(
                      M, N, m0, n0, code_ld, scale_ld, wm, wn, h, l32);
   }
 
-  // ---- epilogue: alpha * acc -> BF16, staged per wave through LDS.
-  // Lane holds output row m = 32 mi + l32 and columns n = 32 ni + 8 q + 4 h + e
-  // (e = 0..3) of the wave tile (D = B_tile . A_tile^T layout).
-  const float alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax) * 16384.0f;   // undo 2^-7 per operand
-  uint8_t* E = smem + wave * (128 * kNvEpiRowB);
+  nv_epilogue(acc, smem, a_amax, b_amax, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
+}
+
+// ---------------------------------------------------------------- ping-pong kernel
+//
+// Same 256 x 256 output tile, wave tiles and FP16 dequant route, scheduled so
+// that the MFMA pipe of every SIMD is fed by one wave while its sibling wave
+// does the memory and dequant work.  The two waves of a SIMD belong to
+// different groups (waves 0-3 and 4-7 share SIMDs pairwise); time is cut into
+// slots separated by workgroup barriers, and in each slot one group runs the
+// 16 MFMAs of a 32-wide K half-stage on fragments already in registers while
+// the other group
+//  * reads its fragments for its next half-stage from LDS,
+//  * expands one operand's 256 rows of a later half-stage to FP16 in LDS
+//    (group 0 the A rows, group 1 the B rows; 32 elements per thread), from
+//    raw codes and scales its own wave staged in LDS, and
+//  * every fourth turn, stages the raw data of four more half-stages with
+//    global -> LDS direct loads.
+// Group 0 computes on even slots and expands half-stage j + 2 on odd ones;
+// group 1 expands half-stage j + 1 on even slots and computes on odd ones, so
+// half-stage t is complete in LDS (A part at slot 2t - 3, B part at 2t - 2)
+// before group 0 reads it (slot 2t - 1) and group 1 reads it (slot 2t), and
+// two FP16 buffers suffice.  Past the last half-stage the staging loads and
+// expansions are clamped to it: those writes land where nobody reads again.
+constexpr int kPpRowB = 80;                      // LDS bytes per row: 32 halves + 16 pad
+constexpr int kPpOpB = 256 * kPpRowB;            // one operand, one half-stage
+constexpr int kPpBufB = 2 * kPpOpB;              // 40960
+static_assert(2 * kPpBufB <= kNvLds, "two half-stage buffers must fit in the LDS allocation");
+
+// Raw operand staging.  Each group stages its operand's 256 rows in LDS, four
+// half-stages (64 code bytes and 8 scale bytes per row) at a time, with
+// global -> LDS direct loads: four lanes cover one row's 64 contiguous code
+// bytes, so a wave instruction touches 16 row segments instead of 64 lines.
+// A wave loads exactly the rows its own threads expand, so only its own
+// vmcnt orders the staging writes and reads.  The 16-byte chunk c of row r sits
+// in slot c ^ ((r >> 2) & 3), which keeps the per-turn reads (one chunk of 64
+// consecutive rows) free of bank conflicts.
+constexpr int kPpStCodeB = 256 * 64;                 // codes of one staged quad
+constexpr int kPpStB = kPpStCodeB + 256 * 8;         // plus scales
+constexpr int kPpStOff = 2 * kPpBufB;                // staging after the FP16 buffers
+constexpr int kPpLds = kPpStOff + 4 * kPpStB;        // 2 groups x 2 staging buffers
+static_assert(kPpLds >= kNvLds && kPpLds <= 160 * 1024, "ping-pong LDS plan");
+
+// Per-lane byte offsets of this lane's direct loads within the operand arrays.
+struct PpLoadMap {
+  uint32_t code[4];                                  // instruction q: 16 rows x 64 bytes
+  uint32_t scale[2];                                 // instruction p: 32 rows x 8 bytes
+};
+
+// One direct load: each lane reads BYTES at base + voff into LDS address
+// lds + lane * BYTES (M0 holds the wave-uniform LDS address).  Written as
+// inline assembly so that the compiler neither waits for it at workgroup
+// fences nor before unrelated LDS reads; pp_wait_staged orders the reads.
+template <int BYTES>
+__device__ __forceinline__ void pp_dma(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  if (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
+// Issue the 6 direct loads of staged quad `qd` (half-stages 4 qd .. 4 qd + 3)
+// into the staging buffer at LDS address `st`: 4 of codes, 2 of scales.
+__device__ __forceinline__ void pp_stage(const uint8_t* codes, const uint8_t* scales,
+                                         const PpLoadMap& lm, int64_t qd, uint32_t st, int w) {
+  const uint8_t* cq = codes + qd * 64;
+  const uint8_t* sq = scales + qd * 8;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int q = 0; q < 4; ++q) pp_dma<16>(cq, lm.code[q], st + (w * 64 + q * 16) * 64);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) pp_dma<4>(sq, lm.scale[p], st + kPpStCodeB + (w * 64 + p * 32) * 8);
+}
+
+// Expand chunk C (0..3) of this thread's staged row into an FP16 LDS row.
+template <int C>
+__device__ __forceinline__ void pp_expand(const uint8_t* st, int r, uint8_t* row) {
+  const uint4 codes = *reinterpret_cast<const uint4*>(st + r * 64 + ((C ^ ((r >> 2) & 3)) << 4));
+  const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kPpStCodeB + r * 8 + (C >> 1) * 4);
+  const halfx2 s0 = nvfp4_scale_pair<2 * (C & 1)>(sw), s1 = nvfp4_scale_pair<2 * (C & 1) + 1>(sw);
+  *reinterpret_cast<halfx8*>(row + 0) = dequant8(codes.x, s0);
+  *reinterpret_cast<halfx8*>(row + 16) = dequant8(codes.y, s0);
+  *reinterpret_cast<halfx8*>(row + 32) = dequant8(codes.z, s1);
+  *reinterpret_cast<halfx8*>(row + 48) = dequant8(codes.w, s1);
+}
+
+// Fragments of one half-stage: 4 A tiles and 2 B tiles of 32 rows, 2 K steps.
+struct PpFrags {
+  halfx8 a[2][4], b[2][2];
+};
+
+__device__ __forceinline__ void pp_frags(PpFrags& f, const uint8_t* buf, int wm, int wn, int h,
+                                         int l32) {
+  const uint8_t* La = buf;
+  const uint8_t* Lb = buf + kPpOpB;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      f.a[s][mi] = *reinterpret_cast<const halfx8*>(La + (wm * 128 + mi * 32 + l32) * kPpRowB + s * 32 + h * 16);
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
+      f.b[s][ni] = *reinterpret_cast<const halfx8*>(Lb + (wn * 64 + ni * 32 + l32) * kPpRowB + s * 32 + h * 16);
+  }
+}
+
+__device__ __forceinline__ void pp_mfma(floatx16 (&acc)[4][2], const PpFrags& f) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t b[4];
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(acc[mi][ni][4 * q + e] * alpha);
-        *reinterpret_cast<uint2*>(E + (mi * 32 + l32) * kNvEpiRowB + (ni * 32 + q * 8 + h * 4) * 2) =
-            make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-      }
-  __syncthreads();
-  const int64_t gm0 = m0 + wm * 128, gn = n0 + wn * 64 + (lane & 7) * 8;
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int row = it * 8 + (lane >> 3);
-    const int64_t gm = gm0 + row;
-    if (gm >= M) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(E + row * kNvEpiRowB + (lane & 7) * 16);
-    uint16_t* dst = c + gm * ldc + gn;
-    if (vec_store && gn + 7 < N) {
-      *reinterpret_cast<uint4*>(dst) = v;
-    } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gn + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[s][ni], f.a[s][mi], acc[mi][ni], 0, 0, 0);
+}
+
+// Workgroup barrier for the ping-pong loops.  Each group runs its own loop
+// (selected by a scalar branch, so no barrier ever sits in an exec-masked
+// region) and both loops pass the same number of barriers per half-stage.
+// Only this wave's LDS operations are waited for: the direct staging loads
+// still in flight are read by their own wave alone, after its explicit vmcnt
+// wait, so the barrier does not wait for them (a workgroup release fence
+// would).  The memory clobber keeps the compiler from moving LDS accesses
+// across the barrier; the scheduling barriers keep the MFMAs inside their slot.
+__device__ __forceinline__ void pp_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wait until at most N of this wave's direct staging loads are in flight.
+template <int N>
+__device__ __forceinline__ void pp_wait_staged() {
+  if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Group 0, half-stage j = 4 J + U: MFMAs of j, then fragments of j + 1 and the
+// A rows of half-stage j + 2 (staged quad J + (U + 2) / 4, chunk (U + 2) % 4)
+// into FP16 buffer U & 1; at U == 2 the quad J + 2 is staged (its buffer held
+// quad J, whose last chunk this group expanded at U == 1).
+template <int U>
+__device__ __forceinline__ void pp_turn0(floatx16 (&acc)[4][2], PpFrags& f, uint8_t* smem,
+                                         uint32_t smem_lds, int64_t J, int64_t NQ,
+                                         const uint8_t* codes, const uint8_t* scales,
+                                         const PpLoadMap& lm, int w, int r, int dst_off, int wm,
+                                         int wn, int h, int l32) {
+  pp_mfma(acc, f);
+  pp_sync();
+  pp_frags(f, smem + ((U + 1) & 1) * kPpBufB, wm, wn, h, l32);
+  const int64_t qd = J + ((U + 2) >> 2);
+  if (U == 2) pp_wait_staged<0>();                  // first read of quad J + 1 (staged 4 turns ago)
+  pp_expand<(U + 2) & 3>(smem + kPpStOff + (qd & 1) * kPpStB, r, smem + (U & 1) * kPpBufB + dst_off);
+  if (U == 2) {
+    const int64_t nq = J + 2 < NQ ? J + 2 : NQ - 1;
+    pp_stage(codes, scales, lm, nq, smem_lds + kPpStOff + (uint32_t)(J & 1) * kPpStB, w);
+  }
+  pp_sync();
+}
+
+// Group 1, half-stage j = 4 J + U: fragments of j, the B rows of half-stage
+// j + 1 into FP16 buffer (U + 1) & 1 (staging two buffers past group 0's), at
+// U == 3 the quad J + 2 is staged; then the MFMAs of j.
+template <int U>
+__device__ __forceinline__ void pp_turn1(floatx16 (&acc)[4][2], PpFrags& f, uint8_t* smem,
+                                         uint32_t smem_lds, int64_t J, int64_t NQ,
+                                         const uint8_t* codes, const uint8_t* scales,
+                                         const PpLoadMap& lm, int w, int r, int dst_off, int wm,
+                                         int wn, int h, int l32) {
+  pp_frags(f, smem + (U & 1) * kPpBufB, wm, wn, h, l32);
+  const int64_t qd = J + ((U + 1) >> 2);
+  if (U == 3) pp_wait_staged<0>();                  // first read of quad J + 1 (staged 4 turns ago)
+  pp_expand<(U + 1) & 3>(smem + kPpStOff + (2 + (qd & 1)) * kPpStB, r,
+                         smem + ((U + 1) & 1) * kPpBufB + dst_off);
+  if (U == 3) {
+    const int64_t nq = J + 2 < NQ ? J + 2 : NQ - 1;
+    pp_stage(codes, scales, lm, nq, smem_lds + kPpStOff + (2 + (uint32_t)(J & 1)) * kPpStB, w);
+  }
+  pp_sync();
+  pp_mfma(acc, f);
+  pp_sync();
+}
+
+__global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_pp(
+    int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+    const float* __restrict__ a_amax, const uint8_t* b_codes, const uint8_t* b_scales,
+    const float* __restrict__ b_amax, uint16_t* __restrict__ c, int64_t ldc, int tiles_m,
+    int tiles_n, int vec_store) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = wave >> 2;
+  const int wm = g, wn = wave & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t code_ld = K / 2, scale_ld = K / 16;
+  const int64_t HT = K / 32;
+
+  // the operand and row this thread expands; its wave stages that row itself
+  // (group and wave index made scalar: they address the direct loads)
+  const int gs = __builtin_amdgcn_readfirstlane(g);
+  const int r = t & 255, w = __builtin_amdgcn_readfirstlane((t >> 6) & 3);
+  const int64_t base = gs == 0 ? m0 : n0, rows = gs == 0 ? M : N;
+  const uint8_t* codes = gs == 0 ? a_codes : b_codes;
+  const uint8_t* scales = gs == 0 ? a_scales : b_scales;
+  PpLoadMap lm;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rr = w * 64 + q * 16 + (lane >> 2);                 // row within the group's 256
+    const int64_t gr = base + rr < rows ? base + rr : rows - 1;  // rows past the end re-read the last
+    const int chunk = (lane & 3) ^ ((rr >> 2) & 3);
+    lm.code[q] = (uint32_t)(gr * code_ld + chunk * 16);
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int rr = w * 64 + p * 32 + (lane >> 1);
+    const int64_t gr = base + rr < rows ? base + rr : rows - 1;
+    lm.scale[p] = (uint32_t)(gr * scale_ld + (lane & 1) * 4);
+  }
+  const int dst_off = gs * kPpOpB + r * kPpRowB;
+  const int64_t NQ = HT / 4;                                      // staged quads
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
+
+  PpFrags f;
+  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  uint8_t* st = smem + kPpStOff + 2 * gs * kPpStB;                // this group's two staging buffers
+  const uint32_t st_lds = smem_lds + kPpStOff + 2 * (uint32_t)gs * kPpStB;
+  pp_stage(codes, scales, lm, 0, st_lds, w);
+  pp_stage(codes, scales, lm, NQ > 1 ? 1 : 0, st_lds + kPpStB, w);
+  pp_wait_staged<6>();                                            // quad 0 in (quad 1 may be in flight)
+  if (gs == 0) {
+    pp_expand<0>(st, r, smem + dst_off);
+    pp_expand<1>(st, r, smem + kPpBufB + dst_off);
+    pp_sync();
+    pp_frags(f, smem, wm, wn, h, l32);
+    for (int64_t J = 0; J < NQ; ++J) {
+      pp_turn0<0>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+      pp_turn0<1>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+      pp_turn0<2>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+      pp_turn0<3>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+    }
+  } else {
+    pp_expand<0>(st, r, smem + dst_off);
+    pp_sync();
+    for (int64_t J = 0; J < NQ; ++J) {
+      pp_turn1<0>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+      pp_turn1<1>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+      pp_turn1<2>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+      pp_turn1<3>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
     }
   }
+  // the last staged loads (clamped re-reads) land in LDS the epilogue reuses
+  pp_wait_staged<0>();
+  pp_sync();
+
+  nv_epilogue(acc, smem, a_amax, b_amax, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
 }
 
 }  // namespace
@@ -261,12 +533,16 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                              const float* ba, void* c, int64_t ldc, hipStream_t s) {
   const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
   const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
-  const bool fast = (K % 64 == 0) && al(ac, 16) && al(bc, 16) && al(as, 2) && al(bs, 2);
+  // the ping-pong kernel stages 64 code bytes and 8 scale bytes per row and four
+  // half-stages, and runs its loop in groups of four half-stages
+  // the staging loads address each operand with 32-bit byte offsets
+  const bool fast = K > 0 && (K % 128 == 0) && al(ac, 16) && al(bc, 16) && al(as, 4) && al(bs, 4) &&
+                    M * (K / 2) < ((int64_t)1 << 32) && N * (K / 2) < ((int64_t)1 << 32);
   const bool vec_store = (ldc % 8 == 0) && al(c, 16);
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kNvLds) != hipSuccess ||
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4_pp),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPpLds) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kNvLds) != hipSuccess)
       return hipErrorInvalidConfiguration;
@@ -275,7 +551,7 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kNvThreads);
   uint16_t* cp = static_cast<uint16_t*>(c);
   if (fast)
-    hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, block, kNvLds, s, M, N, K, ac, as, aa, bc, bs, ba,
+    hipLaunchKernelGGL(k_gemm_nvfp4_pp, grid, block, kPpLds, s, M, N, K, ac, as, aa, bc, bs, ba,
                        cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
   else
     hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, block, kNvLds, s, M, N, K, ac, as, aa, bc, bs, ba,
