@@ -334,16 +334,42 @@ __device__ __forceinline__ void pp_stage(const uint8_t* codes, const uint8_t* sc
   for (int p = 0; p < 2; ++p) pp_dma<4>(sq, lm.scale[p], st + kPpStCodeB + (w * 64 + p * 32) * 8);
 }
 
-// Expand chunk C (0..3) of this thread's staged row into an FP16 LDS row.
+// Chunk C (0..3) of this thread's staged row: codes and the scale dword.
+struct PpRaw {
+  uint4 codes;
+  uint32_t sw;
+};
 template <int C>
-__device__ __forceinline__ void pp_expand(const uint8_t* st, int r, uint8_t* row) {
-  const uint4 codes = *reinterpret_cast<const uint4*>(st + r * 64 + ((C ^ ((r >> 2) & 3)) << 4));
-  const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kPpStCodeB + r * 8 + (C >> 1) * 4);
-  const halfx2 s0 = nvfp4_scale_pair<2 * (C & 1)>(sw), s1 = nvfp4_scale_pair<2 * (C & 1) + 1>(sw);
-  *reinterpret_cast<halfx8*>(row + 0) = dequant8(codes.x, s0);
-  *reinterpret_cast<halfx8*>(row + 16) = dequant8(codes.y, s0);
-  *reinterpret_cast<halfx8*>(row + 32) = dequant8(codes.z, s1);
-  *reinterpret_cast<halfx8*>(row + 48) = dequant8(codes.w, s1);
+__device__ __forceinline__ PpRaw pp_raw(const uint8_t* st, int r) {
+  PpRaw x;
+  x.codes = *reinterpret_cast<const uint4*>(st + r * 64 + ((C ^ ((r >> 2) & 3)) << 4));
+  x.sw = *reinterpret_cast<const uint32_t*>(st + kPpStCodeB + r * 8 + (C >> 1) * 4);
+  return x;
+}
+
+// Expand a staged chunk (half-stage parity Q selects its scale bytes) into an
+// FP16 LDS row.
+template <int Q>
+__device__ __forceinline__ void pp_expand(const PpRaw& x, uint8_t* row) {
+  const halfx2 s0 = nvfp4_scale_pair<2 * Q>(x.sw), s1 = nvfp4_scale_pair<2 * Q + 1>(x.sw);
+  *reinterpret_cast<halfx8*>(row + 0) = dequant8(x.codes.x, s0);
+  *reinterpret_cast<halfx8*>(row + 16) = dequant8(x.codes.y, s0);
+  *reinterpret_cast<halfx8*>(row + 32) = dequant8(x.codes.z, s1);
+  *reinterpret_cast<halfx8*>(row + 48) = dequant8(x.codes.w, s1);
+}
+
+// Memory-slot order: the staged chunk is read first (a scheduling barrier
+// follows its two reads) so that its expansion can start after one LDS
+// latency; the 12 fragment reads then stream through the LDS pipe between the
+// expansion's VALU work, and the 4 FP16 row writes come last.
+__device__ __forceinline__ void pp_mem_order() {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // 3 fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);    // rest of the VALU
+  __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);     // 4 DS writes
 }
 
 // Fragments of one half-stage: 4 A tiles and 2 B tiles of 32 rows, 2 K steps.
@@ -409,10 +435,13 @@ __device__ __forceinline__ void pp_turn0(floatx16 (&acc)[4][2], PpFrags& f, uint
                                          int wn, int h, int l32) {
   pp_mfma(acc, f);
   pp_sync();
-  pp_frags(f, smem + ((U + 1) & 1) * kPpBufB, wm, wn, h, l32);
   const int64_t qd = J + ((U + 2) >> 2);
   if (U == 2) pp_wait_staged<0>();                  // first read of quad J + 1 (staged 4 turns ago)
-  pp_expand<(U + 2) & 3>(smem + kPpStOff + (qd & 1) * kPpStB, r, smem + (U & 1) * kPpBufB + dst_off);
+  const PpRaw raw = pp_raw<(U + 2) & 3>(smem + kPpStOff + (qd & 1) * kPpStB, r);
+  __builtin_amdgcn_sched_barrier(0);
+  pp_frags(f, smem + ((U + 1) & 1) * kPpBufB, wm, wn, h, l32);
+  pp_expand<U & 1>(raw, smem + (U & 1) * kPpBufB + dst_off);
+  pp_mem_order();
   if (U == 2) {
     const int64_t nq = J + 2 < NQ ? J + 2 : NQ - 1;
     pp_stage(codes, scales, lm, nq, smem_lds + kPpStOff + (uint32_t)(J & 1) * kPpStB, w);
@@ -429,11 +458,13 @@ __device__ __forceinline__ void pp_turn1(floatx16 (&acc)[4][2], PpFrags& f, uint
                                          const uint8_t* codes, const uint8_t* scales,
                                          const PpLoadMap& lm, int w, int r, int dst_off, int wm,
                                          int wn, int h, int l32) {
-  pp_frags(f, smem + (U & 1) * kPpBufB, wm, wn, h, l32);
   const int64_t qd = J + ((U + 1) >> 2);
   if (U == 3) pp_wait_staged<0>();                  // first read of quad J + 1 (staged 4 turns ago)
-  pp_expand<(U + 1) & 3>(smem + kPpStOff + (2 + (qd & 1)) * kPpStB, r,
-                         smem + ((U + 1) & 1) * kPpBufB + dst_off);
+  const PpRaw raw = pp_raw<(U + 1) & 3>(smem + kPpStOff + (2 + (qd & 1)) * kPpStB, r);
+  __builtin_amdgcn_sched_barrier(0);
+  pp_frags(f, smem + (U & 1) * kPpBufB, wm, wn, h, l32);
+  pp_expand<(U + 1) & 1>(raw, smem + ((U + 1) & 1) * kPpBufB + dst_off);
+  pp_mem_order();
   if (U == 3) {
     const int64_t nq = J + 2 < NQ ? J + 2 : NQ - 1;
     pp_stage(codes, scales, lm, nq, smem_lds + kPpStOff + (2 + (uint32_t)(J & 1)) * kPpStB, w);
@@ -499,8 +530,8 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_pp(
   pp_stage(codes, scales, lm, NQ > 1 ? 1 : 0, st_lds + kPpStB, w);
   pp_wait_staged<6>();                                            // quad 0 in (quad 1 may be in flight)
   if (gs == 0) {
-    pp_expand<0>(st, r, smem + dst_off);
-    pp_expand<1>(st, r, smem + kPpBufB + dst_off);
+    pp_expand<0>(pp_raw<0>(st, r), smem + dst_off);
+    pp_expand<1>(pp_raw<1>(st, r), smem + kPpBufB + dst_off);
     pp_sync();
     pp_frags(f, smem, wm, wn, h, l32);
     for (int64_t J = 0; J < NQ; ++J) {
@@ -510,7 +541,7 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_pp(
       pp_turn0<3>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
     }
   } else {
-    pp_expand<0>(st, r, smem + dst_off);
+    pp_expand<0>(pp_raw<0>(st, r), smem + dst_off);
     pp_sync();
     for (int64_t J = 0; J < NQ; ++J) {
       pp_turn1<0>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
