@@ -360,15 +360,16 @@ __device__ __forceinline__ void pp_expand(const PpRaw& x, uint8_t* row) {
 
 // Memory-slot order: the staged chunk is read first (a scheduling barrier
 // follows its two reads) so that its expansion can start after one LDS
-// latency; the 12 fragment reads then stream through the LDS pipe between the
+// latency; the fragment reads then stream through the LDS pipe between the
 // expansion's VALU work, and the 4 FP16 row writes come last.
 __device__ __forceinline__ void pp_mem_order() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // 3 fragment reads
+  for (int i = 0; i < 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 fragment reads
     __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
   }
-  __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);    // rest of the VALU
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);    // rest of the VALU
   __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);     // 4 DS writes
 }
 
@@ -377,29 +378,32 @@ struct PpFrags {
   halfx8 a[2][4], b[2][2];
 };
 
+// Fragment reads of K step S: A tiles (PART & 1) and/or B tiles (PART & 2).
+template <int S, int PART>
 __device__ __forceinline__ void pp_frags(PpFrags& f, const uint8_t* buf, int wm, int wn, int h,
                                          int l32) {
   const uint8_t* La = buf;
   const uint8_t* Lb = buf + kPpOpB;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  if (PART & 1) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
-      f.a[s][mi] = *reinterpret_cast<const halfx8*>(La + (wm * 128 + mi * 32 + l32) * kPpRowB + s * 32 + h * 16);
+      f.a[S][mi] = *reinterpret_cast<const halfx8*>(La + (wm * 128 + mi * 32 + l32) * kPpRowB + S * 32 + h * 16);
+  }
+  if (PART & 2) {
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
-      f.b[s][ni] = *reinterpret_cast<const halfx8*>(Lb + (wn * 64 + ni * 32 + l32) * kPpRowB + s * 32 + h * 16);
+      f.b[S][ni] = *reinterpret_cast<const halfx8*>(Lb + (wn * 64 + ni * 32 + l32) * kPpRowB + S * 32 + h * 16);
   }
 }
 
+// The 8 MFMAs of K step S.
+template <int S>
 __device__ __forceinline__ void pp_mfma(floatx16 (&acc)[4][2], const PpFrags& f) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[s][ni], f.a[s][mi], acc[mi][ni], 0, 0, 0);
+    for (int ni = 0; ni < 2; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[S][ni], f.a[S][mi], acc[mi][ni], 0, 0, 0);
 }
 
 // Workgroup barrier for the ping-pong loops.  Each group runs its own loop
@@ -426,20 +430,28 @@ __device__ __forceinline__ void pp_wait_staged() {
 // Group 0, half-stage j = 4 J + U: MFMAs of j, then fragments of j + 1 and the
 // A rows of half-stage j + 2 (staged quad J + (U + 2) / 4, chunk (U + 2) % 4)
 // into FP16 buffer U & 1; at U == 2 the quad J + 2 is staged (its buffer held
-// quad J, whose last chunk this group expanded at U == 1).
+// quad J, whose last chunk this group expanded at U == 1).  Between its two
+// K steps of MFMAs the group already reads the step-0 A fragments of j + 1:
+// those rows are its own, written in its previous memory slot.
 template <int U>
 __device__ __forceinline__ void pp_turn0(floatx16 (&acc)[4][2], PpFrags& f, uint8_t* smem,
                                          uint32_t smem_lds, int64_t J, int64_t NQ,
                                          const uint8_t* codes, const uint8_t* scales,
                                          const PpLoadMap& lm, int w, int r, int dst_off, int wm,
                                          int wn, int h, int l32) {
-  pp_mfma(acc, f);
+  const uint8_t* nxt = smem + ((U + 1) & 1) * kPpBufB;      // half-stage j + 1
+  pp_mfma<0>(acc, f);
+  __builtin_amdgcn_sched_barrier(0);
+  pp_frags<0, 1>(f, nxt, wm, wn, h, l32);
+  __builtin_amdgcn_sched_barrier(0);
+  pp_mfma<1>(acc, f);
   pp_sync();
   const int64_t qd = J + ((U + 2) >> 2);
   if (U == 2) pp_wait_staged<0>();                  // first read of quad J + 1 (staged 4 turns ago)
   const PpRaw raw = pp_raw<(U + 2) & 3>(smem + kPpStOff + (qd & 1) * kPpStB, r);
   __builtin_amdgcn_sched_barrier(0);
-  pp_frags(f, smem + ((U + 1) & 1) * kPpBufB, wm, wn, h, l32);
+  pp_frags<0, 2>(f, nxt, wm, wn, h, l32);
+  pp_frags<1, 3>(f, nxt, wm, wn, h, l32);
   pp_expand<U & 1>(raw, smem + (U & 1) * kPpBufB + dst_off);
   pp_mem_order();
   if (U == 2) {
@@ -449,9 +461,11 @@ __device__ __forceinline__ void pp_turn0(floatx16 (&acc)[4][2], PpFrags& f, uint
   pp_sync();
 }
 
-// Group 1, half-stage j = 4 J + U: fragments of j, the B rows of half-stage
-// j + 1 into FP16 buffer (U + 1) & 1 (staging two buffers past group 0's), at
-// U == 3 the quad J + 2 is staged; then the MFMAs of j.
+// Group 1, half-stage j = 4 J + U: step-1 fragments of j (step 0 was read
+// during the previous MFMA slot), the B rows of half-stage j + 1 into FP16
+// buffer (U + 1) & 1 (staging two buffers past group 0's), at U == 3 the quad
+// J + 2 is staged; then the MFMAs of j, reading the step-0 fragments of j + 1
+// between the two K steps (both operands of j + 1 are complete by then).
 template <int U>
 __device__ __forceinline__ void pp_turn1(floatx16 (&acc)[4][2], PpFrags& f, uint8_t* smem,
                                          uint32_t smem_lds, int64_t J, int64_t NQ,
@@ -462,7 +476,7 @@ __device__ __forceinline__ void pp_turn1(floatx16 (&acc)[4][2], PpFrags& f, uint
   if (U == 3) pp_wait_staged<0>();                  // first read of quad J + 1 (staged 4 turns ago)
   const PpRaw raw = pp_raw<(U + 1) & 3>(smem + kPpStOff + (2 + (qd & 1)) * kPpStB, r);
   __builtin_amdgcn_sched_barrier(0);
-  pp_frags(f, smem + (U & 1) * kPpBufB, wm, wn, h, l32);
+  pp_frags<1, 3>(f, smem + (U & 1) * kPpBufB, wm, wn, h, l32);
   pp_expand<(U + 1) & 1>(raw, smem + ((U + 1) & 1) * kPpBufB + dst_off);
   pp_mem_order();
   if (U == 3) {
@@ -470,7 +484,11 @@ __device__ __forceinline__ void pp_turn1(floatx16 (&acc)[4][2], PpFrags& f, uint
     pp_stage(codes, scales, lm, nq, smem_lds + kPpStOff + (2 + (uint32_t)(J & 1)) * kPpStB, w);
   }
   pp_sync();
-  pp_mfma(acc, f);
+  pp_mfma<0>(acc, f);
+  __builtin_amdgcn_sched_barrier(0);
+  pp_frags<0, 3>(f, smem + ((U + 1) & 1) * kPpBufB, wm, wn, h, l32);
+  __builtin_amdgcn_sched_barrier(0);
+  pp_mfma<1>(acc, f);
   pp_sync();
 }
 
@@ -533,7 +551,8 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_pp(
     pp_expand<0>(pp_raw<0>(st, r), smem + dst_off);
     pp_expand<1>(pp_raw<1>(st, r), smem + kPpBufB + dst_off);
     pp_sync();
-    pp_frags(f, smem, wm, wn, h, l32);
+    pp_frags<0, 3>(f, smem, wm, wn, h, l32);
+    pp_frags<1, 3>(f, smem, wm, wn, h, l32);
     for (int64_t J = 0; J < NQ; ++J) {
       pp_turn0<0>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
       pp_turn0<1>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
@@ -543,6 +562,7 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_pp(
   } else {
     pp_expand<0>(pp_raw<0>(st, r), smem + dst_off);
     pp_sync();
+    pp_frags<0, 3>(f, smem, wm, wn, h, l32);          // step 0 of half-stage 0
     for (int64_t J = 0; J < NQ; ++J) {
       pp_turn1<0>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
       pp_turn1<1>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
