@@ -1,30 +1,24 @@
-// Block-scaled GEMM for gfx950: C[M, N] (BF16) = alpha * A[M, K] . B[N, K]^T.
+// MX block-scaled GEMM for gfx950: C[M, N] (BF16) = A[M, K] . B[N, K]^T with
+// MXFP8 (E4M3) or MXFP4 (E2M1) codes and one E8M0 scale per 32 K-elements.
 //
-// NVFP4 pretraining post, data-flow paragraph after Figure 1: the FPROP, DGRAD
-// and WGRAD GEMMs consume NVFP4 operands and emit BF16.  HN page opcode84: MX
-// formats apply the block scale inside the matrix unit.
+// HN page opcode84 (MXFP8 / MXFP4 GEMMs on the OCP Microscaling formats): the
+// block scale is applied inside the matrix unit.  On CDNA4,
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes one E8M0 scale per lane per 32-element
+// K block, which is exactly the MX block, so codes go from LDS straight into
+// the MFMA (operand layouts in k_gemm_mx below).  The NVFP4 GEMM lives in
+// bsq_gemm_nvfp4.hip.
 //
-// Routes on CDNA4:
-//  * MXFP8 / MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4 takes one E8M0 scale per
-//    lane per 32-element K block, which is exactly the MX block, so codes go
-//    from LDS straight into the MFMA.
-//  * NVFP4: the 16-element E4M3 block scale is not an MFMA scale type.  Each
-//    E2M1 value times an E4M3 scale has at most 6 significant bits and lies in
-//    [2^-10, 2688], so it is exact in FP16 (and BF16): the codes are expanded
-//    in registers to FP16 products (see dequant8) and fed to
-//    v_mfma_f32_32x32x16_f16 (FP32 accumulate).  The per-tensor scales multiply
-//    the FP32 result once.
-//
-// Tiling: 256x256 output tile per 512-thread block (8 waves as 2 x 4, each
-// wave 128 (M) x 64 (N) = 4 x 2 MFMA tiles of 32x32), K stage of 128
-// (NVFP4, MXFP8) or 256 (MXFP4) elements, LDS double buffer, one barrier per
-// stage.  Each wave computes D = B_tile . A_tile^T so that every lane holds 4
-// consecutive output columns of a row (8-byte BF16 stores).
+// Tiling: 256 x 256 output tile per 512-thread workgroup (8 waves as 2 x 4,
+// each 128 (M) x 64 (N) = 4 x 2 MFMA tiles of 32 x 32); each wave computes
+// D = B_tile . A_tile^T so that every lane holds consecutive output columns.
+//  * k_gemm_mx (K % 128 == 0, aligned operands): 64 code bytes per row per
+//    stage (K 64 for MXFP8, 128 for MXFP4) staged in LDS by global -> LDS
+//    direct loads three stages ahead (four stage buffers), one barrier per
+//    stage.
+//  * k_gemm (any K): the general path, register-staged, one stage ahead.
 //
 // K order inside a stage: an MFMA only needs A and B to agree on which K index
-// sits in which slot, so lane half h takes one contiguous run of the stage
-// (NVFP4: elements [64h, 64h+64), 8 per step over 8 steps; MX: one 32-element
-// block per step) and reads it from LDS with 16-byte loads.
+// sits in which slot, so lane half h takes one contiguous run of the stage.
 #include "bsq_gemm_common.hpp"
 #include "bsq_internal.hpp"
 
@@ -294,6 +288,162 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   }
 }
 
+// ---------------------------------------------------------------- staged kernel
+//
+// Stage layout in LDS (34 KiB, four buffers): A codes 256 rows x 64 bytes, B
+// codes the same (16-byte chunk c of row r in slot c ^ ((r >> 2) & 3), which
+// keeps the fragment reads of 16 consecutive rows on distinct banks), then one
+// scale dword per row of A and of B (MXFP8: the dword holding this stage's two
+// scales and the next stage's; MXFP4: this stage's four).  Wave w stages rows
+// 32 w .. 32 w + 31 of both operands' codes (4 direct loads of 16 rows x 64
+// bytes) and the scale dwords of 64 rows of one operand (1 direct load).
+constexpr int kMxRowB = 64;
+constexpr int kMxCodeB = 256 * kMxRowB;
+constexpr int kMxStageB = 2 * kMxCodeB + 2 * 256 * 4;
+constexpr int kMxStages = 4;
+constexpr int kMxLds = kMxStages * kMxStageB > kEpiLds ? kMxStages * kMxStageB : kEpiLds;
+constexpr int kMxDma = 5;                                // direct loads per wave per stage
+static_assert(kMxLds <= 160 * 1024, "MX staged LDS plan");
+
+struct MxLoadMap {
+  uint32_t code[4];                                      // byte offset of this lane's 16 bytes
+  uint32_t scale;                                        // byte offset of this lane's scale row
+};
+
+template <int FMT>
+__device__ __forceinline__ void mx_stage(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
+                                         const uint8_t* bs, const MxLoadMap& lm, int64_t kt,
+                                         uint32_t st, int w) {
+  const int64_t sdw = FMT == kMXFP8 ? (kt >> 1) : kt;     // scale dword index along the row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* base = (i < 2 ? ac : bc) + kt * kMxRowB;
+    dma_to_lds<16>(base, lm.code[i], st + (i >> 1) * kMxCodeB + (w * 32 + (i & 1) * 16) * kMxRowB);
+  }
+  dma_to_lds<4>((w < 4 ? as : bs) + sdw * 4, lm.scale, st + 2 * kMxCodeB + (w >> 2) * 1024 + (w & 3) * 256);
+}
+
+// One stage of MFMAs from LDS buffer `buf`; P = stage parity (MXFP8 scale byte).
+template <int FMT, int P>
+__device__ __forceinline__ void mx_compute(floatx16 (&acc)[4][2], const uint8_t* buf, int wm,
+                                           int wn, int h, int l32) {
+  constexpr int FMTC = FMT == kMXFP8 ? 0 : 4;            // cbsz / blgp operand type
+  const uint8_t* La = buf;
+  const uint8_t* Lb = buf + kMxCodeB;
+  const uint8_t* Sa = buf + 2 * kMxCodeB;
+  const uint8_t* Sb = Sa + 1024;
+  // scale operands: MXFP8 lane half h carries the scale of the instruction's
+  // block h (stage block h, byte 2P + h); MXFP4 lane half h supplies stage
+  // blocks 2h + s (byte 2h + s), selected below by the K step s
+  uint32_t sca[4], scb[2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+    sca[mi] = *reinterpret_cast<const uint32_t*>(Sa + (wm * 128 + mi * 32 + l32) * 4) >> (FMT == kMXFP8 ? 8 * h : 16 * h);
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+    scb[ni] = *reinterpret_cast<const uint32_t*>(Sb + (wn * 64 + ni * 32 + l32) * 4) >> (FMT == kMXFP8 ? 8 * h : 16 * h);
+  const auto chunk = [](const uint8_t* base, int row, int c) {
+    return *reinterpret_cast<const uint4*>(base + row * kMxRowB + ((c ^ ((row >> 2) & 3)) << 4));
+  };
+  constexpr int STEPS = FMT == kMXFP8 ? 1 : 2;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    intx8 fa[4], fb[2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int row = wm * 128 + mi * 32 + l32;
+      // MXFP8: bytes 0-15 = elements [16h, 16h + 16) of block 0 (chunk h),
+      // bytes 16-31 = the same of block 1 (chunk 2 + h); MXFP4: block 2h + s
+      const uint4 lo = chunk(La, row, FMT == kMXFP8 ? h : 2 * h + s);
+      const uint4 hi = FMT == kMXFP8 ? chunk(La, row, 2 + h) : make_uint4(0, 0, 0, 0);
+      fa[mi] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int row = wn * 64 + ni * 32 + l32;
+      const uint4 lo = chunk(Lb, row, FMT == kMXFP8 ? h : 2 * h + s);
+      const uint4 hi = FMT == kMXFP8 ? chunk(Lb, row, 2 + h) : make_uint4(0, 0, 0, 0);
+      fb[ni] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    constexpr int SEL = FMT == kMXFP8 ? 2 * P : 0;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = mfma_mx<FMTC>(FMT == kMXFP8 ? SEL : s, fb[ni], fa[mi], acc[mi][ni], scb[ni], sca[mi]);
+  }
+}
+
+// One stage: wait for it, barrier, stage kt + 3, compute kt.  P = kt & 1
+// (only MXFP8 uses it, to pick the scale bytes of its half of the dword).
+template <int FMT, int P>
+__device__ __forceinline__ void mx_iter(floatx16 (&acc)[4][2], uint8_t* smem, uint32_t smem_lds,
+                                        const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
+                                        const uint8_t* bs, const MxLoadMap& lm, int64_t kt,
+                                        int64_t KT, int w, int wm, int wn, int h, int l32) {
+  wait_vmcnt<2 * kMxDma>();                    // this wave's loads of stage kt are in
+  lds_barrier();                               // everyone's are; stage kt - 1 is read
+  const int64_t nk = kt + 3 < KT ? kt + 3 : KT - 1;
+  mx_stage<FMT>(ac, as, bc, bs, lm, nk, smem_lds + (uint32_t)((kt + 3) & 3) * kMxStageB, w);
+  mx_compute<FMT, P>(acc, smem + (kt & 3) * kMxStageB, wm, wn, h, l32);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_gemm_mx(
+    int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+    const uint8_t* b_codes, const uint8_t* b_scales, uint16_t* __restrict__ c, int64_t ldc,
+    int tiles_m, int tiles_n, int vec_store) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t code_ld = FMT == kMXFP8 ? K : K / 2, scale_ld = K / 32;
+  const int64_t KT = code_ld / kMxRowB;                  // stages
+  MxLoadMap lm;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = w * 32 + (i & 1) * 16 + (lane >> 2);  // row within the tile
+    const int64_t base = i < 2 ? m0 : n0, rows = i < 2 ? M : N;
+    const int64_t gr = base + rr < rows ? base + rr : rows - 1;
+    lm.code[i] = (uint32_t)(gr * code_ld + (((lane & 3) ^ ((rr >> 2) & 3)) << 4));
+  }
+  {
+    const int rr = (w & 3) * 64 + lane;
+    const int64_t base = w < 4 ? m0 : n0, rows = w < 4 ? M : N;
+    const int64_t gr = base + rr < rows ? base + rr : rows - 1;
+    lm.scale = (uint32_t)(gr * scale_ld);
+  }
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    mx_stage<FMT>(a_codes, a_scales, b_codes, b_scales, lm, k < KT ? k : KT - 1,
+                  smem_lds + k * kMxStageB, w);
+  if (FMT == kMXFP8) {                         // KT is even (K % 128 == 0)
+    for (int64_t kt = 0; kt < KT; kt += 2) {
+      mx_iter<FMT, 0>(acc, smem, smem_lds, a_codes, a_scales, b_codes, b_scales, lm, kt, KT, w, wm, wn, h, l32);
+      mx_iter<FMT, 1>(acc, smem, smem_lds, a_codes, a_scales, b_codes, b_scales, lm, kt + 1, KT, w, wm, wn, h, l32);
+    }
+  } else {
+    for (int64_t kt = 0; kt < KT; ++kt)
+      mx_iter<FMT, 0>(acc, smem, smem_lds, a_codes, a_scales, b_codes, b_scales, lm, kt, KT, w, wm, wn, h, l32);
+  }
+  wait_vmcnt<0>();                             // the clamped tail loads land in LDS the epilogue reuses
+  lds_barrier();
+  store_tile_bf16(acc, smem, 1.0f, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
+}
+
 template <int FMT>
 hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                          const float* aa, const uint8_t* bc, const uint8_t* bs, const float* ba,
@@ -319,6 +469,23 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   }
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
   uint16_t* cp = static_cast<uint16_t*>(c);
+  // staged kernel: whole 64-byte code segments and aligned scale dwords per
+  // stage, 32-bit byte offsets within each operand
+  const bool staged = K > 0 && K % 128 == 0 && al16(ac) && al16(bc) &&
+                      ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(bs)) % 4 == 0) &&
+                      M * code_ld < ((int64_t)1 << 32) && N * code_ld < ((int64_t)1 << 32);
+  static bool mx_attr_set = false;
+  if (staged) {
+    if (!mx_attr_set) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx<FMT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds) != hipSuccess)
+        return hipErrorInvalidConfiguration;
+      mx_attr_set = true;
+    }
+    hipLaunchKernelGGL((k_gemm_mx<FMT>), grid, block, kMxLds, s, M, N, K, ac, as, bc, bs, cp, ldc,
+                       tiles_m, tiles_n, vec_store ? 1 : 0);
+    return hipGetLastError();
+  }
   if (fast)
     hipLaunchKernelGGL((k_gemm<FMT, true>), grid, block, lds, s, M, N, K, ac, as, aa, bc, bs, ba,
                        cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);

@@ -75,4 +75,86 @@ __device__ __forceinline__ void tile_of_block(int pid, int tiles_m, int tiles_n,
   tn = (t % group_size) / gm;
 }
 
+// ---------------------------------------------------------------- shared GEMM pieces
+
+// Epilogue of a 512-thread, 256 x 256 tile whose 8 waves (2 x 4) each hold a
+// 128 x 64 accumulator as 4 x 2 MFMA tiles of 32 x 32 in the D = B . A^T
+// layout: alpha * acc -> BF16 RNE, staged per wave through LDS so that global
+// stores are whole 128-byte row segments.  Lane holds output row
+// m = 32 mi + l32 and columns n = 32 ni + 8 q + 4 h + e (e = 0..3) of the wave
+// tile.  The caller has passed a barrier after the last LDS read of its main
+// loop; the staging needs kEpiLds bytes of LDS.
+constexpr int kEpiRowB = 144;                        // LDS bytes per staged 64-wide BF16 row
+constexpr int kEpiLds = 8 * 128 * kEpiRowB;          // 147456
+__device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[4][2], uint8_t* smem,
+                                                float alpha, uint16_t* c, int64_t ldc, int64_t M,
+                                                int64_t N, int64_t m0, int64_t n0, int wm, int wn,
+                                                int lane, int vec_store) {
+  const int h = lane >> 5, l32 = lane & 31, wave = threadIdx.x >> 6;
+  uint8_t* E = smem + wave * (128 * kEpiRowB);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(acc[mi][ni][4 * q + e] * alpha);
+        *reinterpret_cast<uint2*>(E + (mi * 32 + l32) * kEpiRowB + (ni * 32 + q * 8 + h * 4) * 2) =
+            make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      }
+  __syncthreads();
+  const int64_t gm0 = m0 + wm * 128, gn = n0 + wn * 64 + (lane & 7) * 8;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 8 + (lane >> 3);
+    const int64_t gm = gm0 + row;
+    if (gm >= M) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(E + row * kEpiRowB + (lane & 7) * 16);
+    uint16_t* dst = c + gm * ldc + gn;
+    if (vec_store && gn + 7 < N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gn + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+
+// One global -> LDS direct load: each lane reads BYTES (4 or 16) at base + voff
+// into LDS address lds + lane * BYTES; M0 holds the wave-uniform LDS address.
+// Written as inline assembly so that the compiler neither waits for it at
+// workgroup fences nor before unrelated LDS reads; wait_vmcnt orders the
+// reads of the staged data.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  if (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations (here: direct
+// loads) are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations: direct
+// loads in flight are not waited for (a workgroup release fence would wait
+// for them).  The memory clobber keeps the compiler from moving LDS accesses
+// across it; the scheduling barriers keep register-only work (MFMAs) on its
+// side of it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace bsq

@@ -34,8 +34,7 @@ constexpr int kNvRowB = 144;                      // LDS bytes per FP16 row (64 
 constexpr int kNvOpB = 256 * kNvRowB;             // one operand, one stage
 constexpr int kNvStageB = 2 * kNvOpB;
 constexpr int kNvLds = 2 * kNvStageB;             // 147456 bytes
-constexpr int kNvEpiRowB = 144;                   // LDS bytes per row of a wave's 128 x 64 BF16 tile
-static_assert(8 * 128 * kNvEpiRowB <= kNvLds, "epilogue staging must fit in the stage buffers");
+static_assert(kEpiLds <= kNvLds, "epilogue staging must fit in the stage buffers");
 
 // 32 consecutive K-elements of one operand row (two 16-element blocks).
 struct NvChunk {
@@ -51,48 +50,14 @@ __device__ __forceinline__ NvScales nv_scales(const NvChunk& c) {
   return NvScales{nvfp4_scale_pair<0>(c.scales), nvfp4_scale_pair<1>(c.scales)};
 }
 
-// Epilogue shared by both kernels: alpha * acc -> BF16, staged per wave through
-// LDS so that global stores are whole 128-byte row segments.  Lane holds output
-// row m = 32 mi + l32 and columns n = 32 ni + 8 q + 4 h + e (e = 0..3) of the
-// wave's 128 x 64 tile (D = B_tile . A_tile^T layout).  The caller has passed a
-// barrier after the last LDS read of the main loop.
+// Epilogue of both NVFP4 kernels: alpha = s_dec(A) * s_dec(B), times 2^14 to
+// undo the 2^-7 each expanded operand carries.
 __device__ __forceinline__ void nv_epilogue(const floatx16 (&acc)[4][2], uint8_t* smem,
                                             const float* a_amax, const float* b_amax, uint16_t* c,
                                             int64_t ldc, int64_t M, int64_t N, int64_t m0,
                                             int64_t n0, int wm, int wn, int lane, int vec_store) {
-  const int h = lane >> 5, l32 = lane & 31, wave = threadIdx.x >> 6;
-  const float alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax) * 16384.0f;   // undo 2^-7 per operand
-  uint8_t* E = smem + wave * (128 * kNvEpiRowB);
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(acc[mi][ni][4 * q + e] * alpha);
-        *reinterpret_cast<uint2*>(E + (mi * 32 + l32) * kNvEpiRowB + (ni * 32 + q * 8 + h * 4) * 2) =
-            make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-      }
-  __syncthreads();
-  const int64_t gm0 = m0 + wm * 128, gn = n0 + wn * 64 + (lane & 7) * 8;
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int row = it * 8 + (lane >> 3);
-    const int64_t gm = gm0 + row;
-    if (gm >= M) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(E + row * kNvEpiRowB + (lane & 7) * 16);
-    uint16_t* dst = c + gm * ldc + gn;
-    if (vec_store && gn + 7 < N) {
-      *reinterpret_cast<uint4*>(dst) = v;
-    } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gn + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-  }
+  const float alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax) * 16384.0f;
+  store_tile_bf16(acc, smem, alpha, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
 }
 
 // Chunk of thread t for stage kt: row t/2 of the 256-row tile, half t%2 of
@@ -310,18 +275,6 @@ struct PpLoadMap {
   uint32_t scale[2];                                 // instruction p: 32 rows x 8 bytes
 };
 
-// One direct load: each lane reads BYTES at base + voff into LDS address
-// lds + lane * BYTES (M0 holds the wave-uniform LDS address).  Written as
-// inline assembly so that the compiler neither waits for it at workgroup
-// fences nor before unrelated LDS reads; pp_wait_staged orders the reads.
-template <int BYTES>
-__device__ __forceinline__ void pp_dma(const uint8_t* base, uint32_t voff, uint32_t lds) {
-  if (BYTES == 16)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-
 // Issue the 6 direct loads of staged quad `qd` (half-stages 4 qd .. 4 qd + 3)
 // into the staging buffer at LDS address `st`: 4 of codes, 2 of scales.
 __device__ __forceinline__ void pp_stage(const uint8_t* codes, const uint8_t* scales,
@@ -329,9 +282,9 @@ __device__ __forceinline__ void pp_stage(const uint8_t* codes, const uint8_t* sc
   const uint8_t* cq = codes + qd * 64;
   const uint8_t* sq = scales + qd * 8;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) pp_dma<16>(cq, lm.code[q], st + (w * 64 + q * 16) * 64);
+  for (int q = 0; q < 4; ++q) dma_to_lds<16>(cq, lm.code[q], st + (w * 64 + q * 16) * 64);
 #pragma unroll
-  for (int p = 0; p < 2; ++p) pp_dma<4>(sq, lm.scale[p], st + kPpStCodeB + (w * 64 + p * 32) * 8);
+  for (int p = 0; p < 2; ++p) dma_to_lds<4>(sq, lm.scale[p], st + kPpStCodeB + (w * 64 + p * 32) * 8);
 }
 
 // Chunk C (0..3) of this thread's staged row: codes and the scale dword.
@@ -406,26 +359,15 @@ __device__ __forceinline__ void pp_mfma(floatx16 (&acc)[4][2], const PpFrags& f)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[S][ni], f.a[S][mi], acc[mi][ni], 0, 0, 0);
 }
 
-// Workgroup barrier for the ping-pong loops.  Each group runs its own loop
-// (selected by a scalar branch, so no barrier ever sits in an exec-masked
-// region) and both loops pass the same number of barriers per half-stage.
-// Only this wave's LDS operations are waited for: the direct staging loads
-// still in flight are read by their own wave alone, after its explicit vmcnt
-// wait, so the barrier does not wait for them (a workgroup release fence
-// would).  The memory clobber keeps the compiler from moving LDS accesses
-// across the barrier; the scheduling barriers keep the MFMAs inside their slot.
-__device__ __forceinline__ void pp_sync() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
+// Workgroup barrier for the ping-pong loops (see lds_barrier).  Each group
+// runs its own loop (selected by a scalar branch, so no barrier ever sits in
+// an exec-masked region) and both loops pass the same number of barriers per
+// half-stage.  The direct staging loads still in flight are read by their own
+// wave alone, after its explicit vmcnt wait.
+__device__ __forceinline__ void pp_sync() { lds_barrier(); }
 
-// Wait until at most N of this wave's direct staging loads are in flight.
 template <int N>
-__device__ __forceinline__ void pp_wait_staged() {
-  if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
+__device__ __forceinline__ void pp_wait_staged() { wait_vmcnt<N>(); }
 
 // Group 0, half-stage j = 4 J + U: MFMAs of j, then fragments of j + 1 and the
 // A rows of half-stage j + 2 (staged quad J + (U + 2) / 4, chunk (U + 2) % 4)
