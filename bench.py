@@ -12,8 +12,13 @@ One step = the whole hot path of one transformer-MLP layer on one GPU's share
           GEMM dW_gu = dY_gu^T . X
 value = sum(2 M N K) / step time, with BF16 inputs already resident in HBM.
 
+The same step is then timed with the RHT setting flipped (reported as rht_off
+or rht_on), and the MX square workload (4096^3, MXFP8 and MXFP4: mx_quantize of
+both operands + GEMM) is timed on its own and reported with its roofline
+fraction.
+
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--no-rht]
-[--workload 8b|405b] [--no-cpu-baseline].
+[--workload 8b|405b] [--no-cpu-baseline] [--no-mx].
 """
 
 import argparse
@@ -32,6 +37,8 @@ import fp8_quantized_gemm_amd as bsq  # noqa: E402
 from fp8_quantized_gemm_amd import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense BF16 MFMA (the NVFP4 GEMM's matrix path)
+PEAK_FP8_TFLOPS = 5033.2       # dense FP8 MFMA (MXFP8 GEMM)
+PEAK_FP4_TFLOPS = 10066.3      # dense FP4 MFMA (MXFP4 GEMM)
 PEAK_HBM_GBS = 8000.0
 
 NV, MXF4, MXF8 = 0, 1, 2
@@ -131,6 +138,59 @@ class Step:
         timed("WGRAD_gu", lambda: self.gemm(G["WGRAD_gu"]))
 
 
+def mx_square(device, reps=20):
+    """The MX workload (4096 x 4096 x 4096, A and B N(0,1) with outliers):
+    rowwise mx_quantize of both operands, then the block-scaled GEMM, for MXFP8
+    and MXFP4.  Median of `reps` timed repetitions of each call (HIP events on
+    the launch stream)."""
+    lib = bsq.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    A = synth.workload_tensor("mx", "A", device)
+    B = synth.workload_tensor("mx", "B", device)
+    M, K = A.shape
+    N = B.shape[0]
+    out = {}
+    for fmt, fcode, peak in (("mxfp8", MXF8, PEAK_FP8_TFLOPS), ("mxfp4", MXF4, PEAK_FP4_TFLOPS)):
+        cw = K if fmt == "mxfp8" else K // 2
+        ac = torch.empty((M, cw), dtype=torch.uint8, device=device)
+        bc = torch.empty((N, cw), dtype=torch.uint8, device=device)
+        as_ = torch.empty((M, K // 32), dtype=torch.uint8, device=device)
+        bs = torch.empty((N, K // 32), dtype=torch.uint8, device=device)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+
+        def quant():
+            for x, c_, s_ in ((A, ac, as_), (B, bc, bs)):
+                st = lib.mx_quantize(P(x), x.shape[0], K, fcode, RNE, 0, 0, P(c_), P(s_), stream)
+                assert st == 0, bsq.status_string(st)
+
+        def gemm():
+            st = lib.bs_gemm(fcode, M, N, K, P(ac), P(as_), None, P(bc), P(bs), None, P(C), N, stream)
+            assert st == 0, bsq.status_string(st)
+
+        def median_ms(fn):
+            for _ in range(3):
+                fn()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            v = sorted(a.elapsed_time(b) for a, b in ts)
+            return v[len(v) // 2]
+
+        q_ms, g_ms = median_ms(quant), median_ms(gemm)
+        tf = 2.0 * M * N * K / (g_ms * 1e-3) / 1e12
+        qbytes = 2 * (M + N) * K + (M + N) * (cw + K // 32)
+        out[fmt] = {"gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 1),
+                    "gemm_frac_of_peak": round(tf / peak, 4), "peak_tflops": peak,
+                    "quant_ms": round(q_ms, 4), "quant_gbs": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+                    "tflops_incl_quant": round(2.0 * M * N * K / ((g_ms + q_ms) * 1e-3) / 1e12, 1)}
+    return out
+
+
 def gemm_traffic(workload):
     """HBM bytes per k_gemm_nvfp4 launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary of this workload, or None when the kernel sources have
@@ -149,8 +209,8 @@ def gemm_traffic(workload):
 
 
 def cpu_baseline(workload, rht):
-    """The oracle on a bounded slice of the same workload: FPROP_gu for the first
-    TOK tokens and the first NOUT output features (quantize X rows 1x16 RNE,
+    """The oracle on a bounded slice of the same workload (about 10 s of host
+    work): FPROP_gu for the first TOK tokens and the first NOUT output features (quantize X rows 1x16 RNE,
     W_gu rows 16x16 RNE, FP64 GEMM), with the per-tensor amax of both full
     tensors.  Reports TFLOP/s of that slice."""
     import numpy as np
@@ -161,7 +221,7 @@ def cpu_baseline(workload, rht):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         blas_threads = os.cpu_count() or 1
-    TOK, NOUT = 1024, 4096
+    TOK, NOUT = 4096, 12288
     X = synth.workload_tensor(workload, "X", "cpu")
     W = synth.workload_tensor(workload, "W_gu", "cpu")
     bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -191,6 +251,7 @@ def main():
     ap.add_argument("--workload", default="8b", choices=["8b", "405b"])
     ap.add_argument("--no-rht", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MX square-GEMM lines")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path "
@@ -217,6 +278,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / args.steps
+
+    # the same step with RHT off on the WGRAD operands (only the quantizers change)
+    step.rht = 1 - step.rht
+    for _ in range(max(1, args.warmup)):
+        step.run()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record()
+    for _ in range(args.steps):
+        step.run()
+    r1.record()
+    torch.cuda.synchronize()
+    step.rht = 1 - step.rht
+    ms_other = r0.elapsed_time(r1) / args.steps
 
     per = {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in ev.items()}
     gemm_names = [g[0] for g in step.gemms]
@@ -256,8 +332,13 @@ def main():
                      "traffic": gemm_traffic(args.workload),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)"},
         "breakdown": breakdown,
+        ("rht_off" if not args.no_rht else "rht_on"): {
+            "ms_per_step": round(ms_other, 4),
+            "value": round(step.flops / (ms_other * 1e-3) / 1e12, 2)},
         "wall_s": round(wall, 3),
     }
+    if not args.no_mx:
+        out["mx_square_4096"] = mx_square(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, not args.no_rht)
     print(json.dumps(out))
