@@ -233,27 +233,26 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4(
 //
 // Same 256 x 256 output tile, wave tiles and FP16 dequant route, scheduled so
 // that the MFMA pipe of every SIMD is fed by one wave while its sibling wave
-// does the memory and dequant work.  The two waves of a SIMD belong to
-// different groups (waves 0-3 and 4-7 share SIMDs pairwise); time is cut into
-// slots separated by workgroup barriers, and in each slot one group runs the
-// 16 MFMAs of a 32-wide K half-stage on fragments already in registers while
-// the other group
-//  * reads its fragments for its next half-stage from LDS,
-//  * expands one operand's 256 rows of a later half-stage to FP16 in LDS
-//    (group 0 the A rows, group 1 the B rows; 32 elements per thread), from
-//    raw codes and scales its own wave staged in LDS, and
+// does the memory work.  The two waves of a SIMD belong to different groups
+// (waves 0-3 and 4-7 share SIMDs pairwise); time is cut into slots separated
+// by workgroup barriers.  In each slot one group runs the 16 MFMAs of a
+// 32-wide K half-stage on fragments already in registers and, in the shadow of
+// those MFMAs, expands one operand's 256 rows of a later half-stage to FP16 in
+// LDS (group 0 the A rows, group 1 the B rows; 32 elements per thread, from
+// raw codes and scales its own wave staged in LDS), while the other group
+//  * reads all its fragments for its next half-stage from LDS,
+//  * reads the raw chunk its next MFMA slot expands, and
 //  * every fourth turn, stages the raw data of four more half-stages with
 //    global -> LDS direct loads.
-// Group 0 computes on even slots and expands half-stage j + 2 on odd ones;
-// group 1 expands half-stage j + 1 on even slots and computes on odd ones, so
-// half-stage t is complete in LDS (A part at slot 2t - 3, B part at 2t - 2)
-// before group 0 reads it (slot 2t - 1) and group 1 reads it (slot 2t), and
-// two FP16 buffers suffice.  Past the last half-stage the staging loads and
-// expansions are clamped to it: those writes land where nobody reads again.
+// Group 0 computes half-stage j on slot 2j and expands A(j + 1) there; group 1
+// computes j on slot 2j + 1 and expands B(j + 2) there.  So A(j) is complete
+// at slot 2j - 2 and B(j) at slot 2j - 3, before group 0 reads half-stage j
+// (slot 2j - 1) and group 1 reads it (slot 2j), and two FP16 buffers suffice.
+// Past the last half-stage the staging loads and expansions are clamped to
+// it: those writes land where nobody reads again.
 constexpr int kPpRowB = 80;                      // LDS bytes per row: 32 halves + 16 pad
 constexpr int kPpOpB = 256 * kPpRowB;            // one operand, one half-stage
 constexpr int kPpBufB = 2 * kPpOpB;              // 40960
-static_assert(2 * kPpBufB <= kNvLds, "two half-stage buffers must fit in the LDS allocation");
 
 // Raw operand staging.  Each group stages its operand's 256 rows in LDS, four
 // half-stages (64 code bytes and 8 scale bytes per row) at a time, with
@@ -267,24 +266,33 @@ constexpr int kPpStCodeB = 256 * 64;                 // codes of one staged quad
 constexpr int kPpStB = kPpStCodeB + 256 * 8;         // plus scales
 constexpr int kPpStOff = 2 * kPpBufB;                // staging after the FP16 buffers
 constexpr int kPpLds = kPpStOff + 4 * kPpStB;        // 2 groups x 2 staging buffers
-static_assert(kPpLds >= kNvLds && kPpLds <= 160 * 1024, "ping-pong LDS plan");
+static_assert(2 * kPpBufB <= kNvLds, "two half-stage buffers must fit in the LDS allocation");
+static_assert(kPpLds >= kEpiLds && kPpLds <= 160 * 1024, "ping-pong LDS plan");
 
-// Per-lane byte offsets of this lane's direct loads within the operand arrays.
-struct PpLoadMap {
-  uint32_t code[4];                                  // instruction q: 16 rows x 64 bytes
-  uint32_t scale[2];                                 // instruction p: 32 rows x 8 bytes
-};
-
-// Issue the 6 direct loads of staged quad `qd` (half-stages 4 qd .. 4 qd + 3)
-// into the staging buffer at LDS address `st`: 4 of codes, 2 of scales.
+// Issue the 6 direct loads of quad `qd` (half-stages 4 qd .. 4 qd + 3) of the
+// 256 operand rows starting at `base` into the staging buffer at LDS address
+// `st`: 4 of codes (16 rows x 64 bytes each), 2 of scales (32 rows x 8 bytes).
+// Rows past `rows` re-read the last row (their results are never stored).
+// The per-lane offsets are formed here, in 32 bits (the operand arrays are
+// below 4 GiB), rather than kept in registers across the loop.
 __device__ __forceinline__ void pp_stage(const uint8_t* codes, const uint8_t* scales,
-                                         const PpLoadMap& lm, int64_t qd, uint32_t st, int w) {
+                                         int64_t base, int64_t rows, int64_t code_ld,
+                                         int64_t scale_ld, int64_t qd, uint32_t st, int w,
+                                         int lane) {
   const uint8_t* cq = codes + qd * 64;
   const uint8_t* sq = scales + qd * 8;
+  const uint32_t b32 = (uint32_t)base, last = (uint32_t)(rows - 1);
+  const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));   // slot c ^ ((r >> 2) & 3)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) dma_to_lds<16>(cq, lm.code[q], st + (w * 64 + q * 16) * 64);
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t gr = min(b32 + (uint32_t)(w * 64 + q * 16 + (lane >> 2)), last);
+    dma_to_lds<16>(cq, gr * (uint32_t)code_ld + chunk * 16, st + (w * 64 + q * 16) * 64);
+  }
 #pragma unroll
-  for (int p = 0; p < 2; ++p) dma_to_lds<4>(sq, lm.scale[p], st + kPpStCodeB + (w * 64 + p * 32) * 8);
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t gr = min(b32 + (uint32_t)(w * 64 + p * 32 + (lane >> 1)), last);
+    dma_to_lds<4>(sq, gr * (uint32_t)scale_ld + (uint32_t)(lane & 1) * 4, st + kPpStCodeB + (w * 64 + p * 32) * 8);
+  }
 }
 
 // Chunk C (0..3) of this thread's staged row: codes and the scale dword.
@@ -301,7 +309,7 @@ __device__ __forceinline__ PpRaw pp_raw(const uint8_t* st, int r) {
 }
 
 // Expand a staged chunk (half-stage parity Q selects its scale bytes) into an
-// FP16 LDS row.
+// FP16 LDS row (prologue only; the main loop interleaves it with MFMAs).
 template <int Q>
 __device__ __forceinline__ void pp_expand(const PpRaw& x, uint8_t* row) {
   const halfx2 s0 = nvfp4_scale_pair<2 * Q>(x.sw), s1 = nvfp4_scale_pair<2 * Q + 1>(x.sw);
@@ -309,21 +317,6 @@ __device__ __forceinline__ void pp_expand(const PpRaw& x, uint8_t* row) {
   *reinterpret_cast<halfx8*>(row + 16) = dequant8(x.codes.y, s0);
   *reinterpret_cast<halfx8*>(row + 32) = dequant8(x.codes.z, s1);
   *reinterpret_cast<halfx8*>(row + 48) = dequant8(x.codes.w, s1);
-}
-
-// Memory-slot order: the staged chunk is read first (a scheduling barrier
-// follows its two reads) so that its expansion can start after one LDS
-// latency; the fragment reads then stream through the LDS pipe between the
-// expansion's VALU work, and the 4 FP16 row writes come last.
-__device__ __forceinline__ void pp_mem_order() {
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 fragment reads
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);    // rest of the VALU
-  __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);     // 4 DS writes
 }
 
 // Fragments of one half-stage: 4 A tiles and 2 B tiles of 32 rows, 2 K steps.
@@ -349,14 +342,66 @@ __device__ __forceinline__ void pp_frags(PpFrags& f, const uint8_t* buf, int wm,
   }
 }
 
-// The 8 MFMAs of K step S.
-template <int S>
-__device__ __forceinline__ void pp_mfma(floatx16 (&acc)[4][2], const PpFrags& f) {
+// One FP16 pair of the expansion: byte SEL of `w` (two E2M1 codes) times the
+// scale pair `s` (see dequant8).
+template <int SEL>
+__device__ __forceinline__ uint32_t pp_pk(uint32_t w, halfx2 s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 0x1p-14f, SEL) * s);
+}
+__device__ __forceinline__ uint32_t pp_pk_sel(uint32_t w, int sel, halfx2 s) {
+  switch (sel) {
+    case 0: return pp_pk<0>(w, s);
+    case 1: return pp_pk<1>(w, s);
+    case 2: return pp_pk<2>(w, s);
+    default: return pp_pk<3>(w, s);
+  }
+}
+
+// Pairs of the expansion issued after MFMA k of a slot: pairs [lo(k), lo(k+1)),
+// spread over MFMAs 2..13 (the scale pairs are formed after MFMAs 0 and 1).
+__host__ __device__ constexpr int pp_pk_lo(int k) {
+  return k < 2 ? 0 : (((k - 2) * 16 + 11) / 12 > 16 ? 16 : ((k - 2) * 16 + 11) / 12);
+}
+
+// MFMA slot: the 16 MFMAs of a half-stage with the expansion of one staged
+// chunk (half-stage parity Q) into the FP16 row `row`, interleaved in program
+// order and pinned there by scheduling barriers, so that the expansion's VALU
+// work issues in the MFMA shadow of the same wave; each 16-byte row write
+// leaves as soon as its 8 values exist, early enough to complete before the
+// slot's barrier.
+template <int Q>
+__device__ __forceinline__ void pp_mfma_slot(floatx16 (&acc)[4][2], const PpFrags& f,
+                                             const PpRaw& raw, uint8_t* row) {
+  const uint32_t cw[4] = {raw.codes.x, raw.codes.y, raw.codes.z, raw.codes.w};
+  halfx2 s0 = {}, s1 = {};
+  uint32_t o[16];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int k = 0; k < 16; ++k) {
+    const int st = k >> 3, mi = (k & 7) >> 1, ni = k & 1;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[st][ni], f.a[st][mi], acc[mi][ni], 0, 0, 0);
+    if (k == 0) s0 = nvfp4_scale_pair<2 * Q>(raw.sw);
+    if (k == 1) s1 = nvfp4_scale_pair<2 * Q + 1>(raw.sw);
+    const int lo = pp_pk_lo(k), hi = pp_pk_lo(k + 1);
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[S][ni], f.a[S][mi], acc[mi][ni], 0, 0, 0);
+    for (int p = 0; p < 16; ++p)
+      if (p >= lo && p < hi) o[p] = pp_pk_sel(cw[p >> 2], p & 3, p < 8 ? s0 : s1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * i + 3 >= lo && 4 * i + 3 < hi)
+        *reinterpret_cast<uint4*>(row + 16 * i) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Memory slot reads: the raw chunk C that the next MFMA slot expands, then all
+// fragments (both K steps) of the half-stage in FP16 buffer `fbuf`.
+template <int C>
+__device__ __forceinline__ void pp_mem_reads(PpFrags& f, PpRaw& raw, const uint8_t* fbuf,
+                                             const uint8_t* st, int r, int wm, int wn, int h,
+                                             int l32) {
+  raw = pp_raw<C>(st, r);
+  pp_frags<0, 3>(f, fbuf, wm, wn, h, l32);
+  pp_frags<1, 3>(f, fbuf, wm, wn, h, l32);
 }
 
 // Workgroup barrier for the ping-pong loops (see lds_barrier).  Each group
@@ -369,68 +414,59 @@ __device__ __forceinline__ void pp_sync() { lds_barrier(); }
 template <int N>
 __device__ __forceinline__ void pp_wait_staged() { wait_vmcnt<N>(); }
 
-// Group 0, half-stage j = 4 J + U: MFMAs of j, then fragments of j + 1 and the
-// A rows of half-stage j + 2 (staged quad J + (U + 2) / 4, chunk (U + 2) % 4)
-// into FP16 buffer U & 1; at U == 2 the quad J + 2 is staged (its buffer held
-// quad J, whose last chunk this group expanded at U == 1).  Between its two
-// K steps of MFMAs the group already reads the step-0 A fragments of j + 1:
-// those rows are its own, written in its previous memory slot.
+// Where a group's staging loads come from (all wave-uniform).
+struct PpSrc {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t base, rows, code_ld, scale_ld;   // the group's 256 operand rows start at `base`
+  int64_t NQ;                              // staged quads (K / 128)
+  uint32_t st_lds;                         // this group's two staging buffers (LDS address)
+  const uint8_t* st;                       // the same, generic pointer
+  int w;                                   // wave within the group
+};
+
+// Staging at U == 2 of quad J: quad J + 2 (clamped to the last) goes into the
+// buffer that held quad J, whose four chunks have been read by now.
+__device__ __forceinline__ void pp_stage_ahead(const PpSrc& s, int64_t J, int lane) {
+  const int64_t qd = J + 2 < s.NQ ? J + 2 : s.NQ - 1;
+  pp_stage(s.codes, s.scales, s.base, s.rows, s.code_ld, s.scale_ld, qd,
+           s.st_lds + (uint32_t)(J & 1) * kPpStB, s.w, lane);
+}
+
+// Group 0, half-stage j = 4 J + U.  Slot 2j: MFMAs of j while expanding
+// A(j + 1) (raw chunk read in the previous slot) into buffer (j + 1) & 1.
+// Slot 2j + 1: fragments of j + 1 (A of j + 1 written in slot 2j, B of j + 1
+// by group 1 in slot 2j - 1) and the raw chunk of A(j + 2); at U == 2 the
+// first chunk of quad J + 1 is read (staged four turns ago) and quad J + 2 is
+// staged.
 template <int U>
-__device__ __forceinline__ void pp_turn0(floatx16 (&acc)[4][2], PpFrags& f, uint8_t* smem,
-                                         uint32_t smem_lds, int64_t J, int64_t NQ,
-                                         const uint8_t* codes, const uint8_t* scales,
-                                         const PpLoadMap& lm, int w, int r, int dst_off, int wm,
-                                         int wn, int h, int l32) {
-  const uint8_t* nxt = smem + ((U + 1) & 1) * kPpBufB;      // half-stage j + 1
-  pp_mfma<0>(acc, f);
-  __builtin_amdgcn_sched_barrier(0);
-  pp_frags<0, 1>(f, nxt, wm, wn, h, l32);
-  __builtin_amdgcn_sched_barrier(0);
-  pp_mfma<1>(acc, f);
+__device__ __forceinline__ void pp_turn0(floatx16 (&acc)[4][2], PpFrags& f, PpRaw& raw,
+                                         uint8_t* smem, const PpSrc& s, int64_t J, int r,
+                                         int dst_off, int wm, int wn, int h, int l32, int lane) {
+  pp_mfma_slot<(U + 1) & 1>(acc, f, raw, smem + ((U + 1) & 1) * kPpBufB + dst_off);
   pp_sync();
-  const int64_t qd = J + ((U + 2) >> 2);
-  if (U == 2) pp_wait_staged<0>();                  // first read of quad J + 1 (staged 4 turns ago)
-  const PpRaw raw = pp_raw<(U + 2) & 3>(smem + kPpStOff + (qd & 1) * kPpStB, r);
-  __builtin_amdgcn_sched_barrier(0);
-  pp_frags<0, 2>(f, nxt, wm, wn, h, l32);
-  pp_frags<1, 3>(f, nxt, wm, wn, h, l32);
-  pp_expand<U & 1>(raw, smem + (U & 1) * kPpBufB + dst_off);
-  pp_mem_order();
-  if (U == 2) {
-    const int64_t nq = J + 2 < NQ ? J + 2 : NQ - 1;
-    pp_stage(codes, scales, lm, nq, smem_lds + kPpStOff + (uint32_t)(J & 1) * kPpStB, w);
-  }
+  if (U == 2) pp_wait_staged<0>();
+  pp_mem_reads<(U + 2) & 3>(f, raw, smem + ((U + 1) & 1) * kPpBufB,
+                            s.st + ((J + ((U + 2) >> 2)) & 1) * kPpStB, r, wm, wn, h, l32);
+  if (U == 2) pp_stage_ahead(s, J, lane);
   pp_sync();
 }
 
-// Group 1, half-stage j = 4 J + U: step-1 fragments of j (step 0 was read
-// during the previous MFMA slot), the B rows of half-stage j + 1 into FP16
-// buffer (U + 1) & 1 (staging two buffers past group 0's), at U == 3 the quad
-// J + 2 is staged; then the MFMAs of j, reading the step-0 fragments of j + 1
-// between the two K steps (both operands of j + 1 are complete by then).
+// Group 1, half-stage j = 4 J + U.  Slot 2j: fragments of j (A of j written by
+// group 0 in slot 2j - 2, B of j by group 1 in slot 2j - 3) and the raw chunk
+// of B(j + 2), with the same staging rule as group 0.  Slot 2j + 1: MFMAs of
+// j while expanding B(j + 2) into buffer j & 1 (whose B(j) both groups have
+// read by then).
 template <int U>
-__device__ __forceinline__ void pp_turn1(floatx16 (&acc)[4][2], PpFrags& f, uint8_t* smem,
-                                         uint32_t smem_lds, int64_t J, int64_t NQ,
-                                         const uint8_t* codes, const uint8_t* scales,
-                                         const PpLoadMap& lm, int w, int r, int dst_off, int wm,
-                                         int wn, int h, int l32) {
-  const int64_t qd = J + ((U + 1) >> 2);
-  if (U == 3) pp_wait_staged<0>();                  // first read of quad J + 1 (staged 4 turns ago)
-  const PpRaw raw = pp_raw<(U + 1) & 3>(smem + kPpStOff + (2 + (qd & 1)) * kPpStB, r);
-  __builtin_amdgcn_sched_barrier(0);
-  pp_frags<1, 3>(f, smem + (U & 1) * kPpBufB, wm, wn, h, l32);
-  pp_expand<(U + 1) & 1>(raw, smem + ((U + 1) & 1) * kPpBufB + dst_off);
-  pp_mem_order();
-  if (U == 3) {
-    const int64_t nq = J + 2 < NQ ? J + 2 : NQ - 1;
-    pp_stage(codes, scales, lm, nq, smem_lds + kPpStOff + (2 + (uint32_t)(J & 1)) * kPpStB, w);
-  }
+__device__ __forceinline__ void pp_turn1(floatx16 (&acc)[4][2], PpFrags& f, PpRaw& raw,
+                                         uint8_t* smem, const PpSrc& s, int64_t J, int r,
+                                         int dst_off, int wm, int wn, int h, int l32, int lane) {
+  if (U == 2) pp_wait_staged<0>();
+  pp_mem_reads<(U + 2) & 3>(f, raw, smem + (U & 1) * kPpBufB,
+                            s.st + ((J + ((U + 2) >> 2)) & 1) * kPpStB, r, wm, wn, h, l32);
+  if (U == 2) pp_stage_ahead(s, J, lane);
   pp_sync();
-  pp_mfma<0>(acc, f);
-  __builtin_amdgcn_sched_barrier(0);
-  pp_frags<0, 3>(f, smem + ((U + 1) & 1) * kPpBufB, wm, wn, h, l32);
-  __builtin_amdgcn_sched_barrier(0);
-  pp_mfma<1>(acc, f);
+  pp_mfma_slot<U & 1>(acc, f, raw, smem + (U & 1) * kPpBufB + dst_off);
   pp_sync();
 }
 
@@ -447,32 +483,24 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_pp(
   const int g = wave >> 2;
   const int wm = g, wn = wave & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t code_ld = K / 2, scale_ld = K / 16;
-  const int64_t HT = K / 32;
 
   // the operand and row this thread expands; its wave stages that row itself
   // (group and wave index made scalar: they address the direct loads)
   const int gs = __builtin_amdgcn_readfirstlane(g);
   const int r = t & 255, w = __builtin_amdgcn_readfirstlane((t >> 6) & 3);
-  const int64_t base = gs == 0 ? m0 : n0, rows = gs == 0 ? M : N;
-  const uint8_t* codes = gs == 0 ? a_codes : b_codes;
-  const uint8_t* scales = gs == 0 ? a_scales : b_scales;
-  PpLoadMap lm;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int rr = w * 64 + q * 16 + (lane >> 2);                 // row within the group's 256
-    const int64_t gr = base + rr < rows ? base + rr : rows - 1;  // rows past the end re-read the last
-    const int chunk = (lane & 3) ^ ((rr >> 2) & 3);
-    lm.code[q] = (uint32_t)(gr * code_ld + chunk * 16);
-  }
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int rr = w * 64 + p * 32 + (lane >> 1);
-    const int64_t gr = base + rr < rows ? base + rr : rows - 1;
-    lm.scale[p] = (uint32_t)(gr * scale_ld + (lane & 1) * 4);
-  }
   const int dst_off = gs * kPpOpB + r * kPpRowB;
-  const int64_t NQ = HT / 4;                                      // staged quads
+  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  PpSrc s;
+  s.codes = gs == 0 ? a_codes : b_codes;
+  s.scales = gs == 0 ? a_scales : b_scales;
+  s.base = gs == 0 ? m0 : n0;
+  s.rows = gs == 0 ? M : N;
+  s.code_ld = K / 2;
+  s.scale_ld = K / 16;
+  s.NQ = K / 128;
+  s.w = w;
+  s.st = smem + kPpStOff + 2 * gs * kPpStB;
+  s.st_lds = smem_lds + kPpStOff + 2 * (uint32_t)gs * kPpStB;
 
   floatx16 acc[4][2];
 #pragma unroll
@@ -483,33 +511,32 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_pp(
       for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
 
   PpFrags f;
-  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  uint8_t* st = smem + kPpStOff + 2 * gs * kPpStB;                // this group's two staging buffers
-  const uint32_t st_lds = smem_lds + kPpStOff + 2 * (uint32_t)gs * kPpStB;
-  pp_stage(codes, scales, lm, 0, st_lds, w);
-  pp_stage(codes, scales, lm, NQ > 1 ? 1 : 0, st_lds + kPpStB, w);
+  PpRaw raw;
+  pp_stage(s.codes, s.scales, s.base, s.rows, s.code_ld, s.scale_ld, 0, s.st_lds, w, lane);
+  pp_stage(s.codes, s.scales, s.base, s.rows, s.code_ld, s.scale_ld, s.NQ > 1 ? 1 : 0,
+           s.st_lds + kPpStB, w, lane);
   pp_wait_staged<6>();                                            // quad 0 in (quad 1 may be in flight)
   if (gs == 0) {
-    pp_expand<0>(pp_raw<0>(st, r), smem + dst_off);
-    pp_expand<1>(pp_raw<1>(st, r), smem + kPpBufB + dst_off);
+    pp_expand<0>(pp_raw<0>(s.st, r), smem + dst_off);             // A(0)
     pp_sync();
+    raw = pp_raw<1>(s.st, r);                                     // A(1), expanded in slot 0
     pp_frags<0, 3>(f, smem, wm, wn, h, l32);
     pp_frags<1, 3>(f, smem, wm, wn, h, l32);
-    for (int64_t J = 0; J < NQ; ++J) {
-      pp_turn0<0>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
-      pp_turn0<1>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
-      pp_turn0<2>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
-      pp_turn0<3>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+    for (int64_t J = 0; J < s.NQ; ++J) {
+      pp_turn0<0>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      pp_turn0<1>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      pp_turn0<2>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      pp_turn0<3>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
     }
   } else {
-    pp_expand<0>(pp_raw<0>(st, r), smem + dst_off);
+    pp_expand<0>(pp_raw<0>(s.st, r), smem + dst_off);             // B(0)
+    pp_expand<1>(pp_raw<1>(s.st, r), smem + kPpBufB + dst_off);   // B(1)
     pp_sync();
-    pp_frags<0, 3>(f, smem, wm, wn, h, l32);          // step 0 of half-stage 0
-    for (int64_t J = 0; J < NQ; ++J) {
-      pp_turn1<0>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
-      pp_turn1<1>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
-      pp_turn1<2>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
-      pp_turn1<3>(acc, f, smem, smem_lds, J, NQ, codes, scales, lm, w, r, dst_off, wm, wn, h, l32);
+    for (int64_t J = 0; J < s.NQ; ++J) {
+      pp_turn1<0>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      pp_turn1<1>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      pp_turn1<2>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      pp_turn1<3>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
     }
   }
   // the last staged loads (clamped re-reads) land in LDS the epilogue reuses
@@ -527,8 +554,8 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
   const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
   const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
   // the ping-pong kernel stages 64 code bytes and 8 scale bytes per row and four
-  // half-stages, and runs its loop in groups of four half-stages
-  // the staging loads address each operand with 32-bit byte offsets
+  // half-stages, runs its loop in groups of four half-stages, and addresses
+  // each operand with 32-bit byte offsets
   const bool fast = K > 0 && (K % 128 == 0) && al(ac, 16) && al(bc, 16) && al(as, 4) && al(bs, 4) &&
                     M * (K / 2) < ((int64_t)1 << 32) && N * (K / 2) < ((int64_t)1 << 32);
   const bool vec_store = (ldc % 8 == 0) && al(c, 16);
@@ -541,8 +568,8 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
       return hipErrorInvalidConfiguration;
     attr_set = true;
   }
-  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kNvThreads);
   uint16_t* cp = static_cast<uint16_t*>(c);
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kNvThreads);
   if (fast)
     hipLaunchKernelGGL(k_gemm_nvfp4_pp, grid, block, kPpLds, s, M, N, K, ac, as, aa, bc, bs, ba,
                        cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
