@@ -130,6 +130,13 @@ __global__ void k_copy_amax(const float* src, float* dst) {
 // ---------------------------------------------------------------- amax passes
 
 constexpr int kAmaxPer = 8;         // chunks per thread per trip (amax pass)
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
+// no swizzle): out-of-range loads return zero.
+constexpr int kBufRsrcWord3 = 0x00020000;
+#ifndef BSQ_AMAX_RHT_BLOCKS
+#define BSQ_AMAX_RHT_BLOCKS 768
+#endif
+constexpr int kAmaxRhtBlocks = BSQ_AMAX_RHT_BLOCKS;   // workgroups of the RHT amax pass (3 per CU)
 
 // Grid-stride amax: each trip a thread loads kAmaxPer 16-byte chunks (a wave
 // reads kAmaxPer runs of 1 KiB) before reducing them; at most 2048 workgroups,
@@ -167,35 +174,92 @@ __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, 
   block_max_atomic(m, a0, a1);
 }
 
-// amax of x and of RHT(x^T): lane owns 8 columns; walks 16-row blocks.
-__global__ __launch_bounds__(256) void k_amax_tile_rht(const uint16_t* __restrict__ x, int64_t R,
-                                                       int64_t C, int gx, int rbs, uint32_t signs,
-                                                       float* amax_row, float* amax_col) {
-  const int bx = blockIdx.x % gx, by = blockIdx.x / gx;
-  const int64_t c0 = ((int64_t)bx * blockDim.x + threadIdx.x) * 8;
-  uint32_t mr = 0, mc = 0;
-  if (c0 < C) {
-    for (int k = 0; k < rbs; ++k) {
-      const int64_t r0 = ((int64_t)by * rbs + k) * 16;
-      if (r0 >= R) break;
-      uint4 v[16];
+// amax of x and of RHT(x^T) for x [R, C] (R % 16 == 0, C % 4 == 0).  A work
+// item is 16 rows x 256 columns, one per wave (a lane owns 4 columns); waves
+// walk the items grid-stride, the next item's 16 row loads in flight while the
+// current one is reduced.
+//  * x amax: BF16 magnitudes compared as packed 16-bit integers.
+//  * RHT amax: the column transform along the 16 rows, with D applied to the
+//    packed BF16 pairs (sign-bit flips) and the 1/4 applied to the final max
+//    (exact: inputs are multiples of 2^-133, so every transformed value is,
+//    and scaling by 1/4 stays in the FP32 range without rounding).
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void amax_rht_item(const uint2 (&v)[16], uint32_t signs, ushort2v& mr,
+                                              float& mc) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * C + c0);
+  for (int i = 0; i < 16; ++i) {
+    mr = __builtin_elementwise_max(mr, __builtin_bit_cast(ushort2v, v[i].x & 0x7FFF7FFFu));
+    mr = __builtin_elementwise_max(mr, __builtin_bit_cast(ushort2v, v[i].y & 0x7FFF7FFFu));
+  }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float y[16];
+  for (int d = 0; d < 2; ++d) {
+    uint32_t s[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = tile_elem(v[i], j);
+    for (int i = 0; i < 16; ++i) s[i] = (d == 0 ? v[i].x : v[i].y) ^ (((signs >> i) & 1u) * 0x80008000u);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mr = max(mr, absbits(y[i]));
-        rht16(y, signs);
+    for (int half = 0; half < 2; ++half) {
+      float y[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mc = max(mc, absbits(y[i]));
+      for (int i = 0; i < 16; ++i) y[i] = half ? bf16_hi(s[i]) : bf16_lo(s[i]);
+#pragma unroll
+      for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if ((i & h) == 0) {
+            const float a = y[i], b = y[i + h];
+            y[i] = a + b;
+            y[i + h] = a - b;
+          }
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mc = fmaxf(mc, fmaxf(fabsf(y[i]), fabsf(y[i + 1])));
     }
   }
-  block_max_atomic(mr, amax_row, nullptr);
-  block_max_atomic(mc, amax_col, nullptr);
+}
+
+// Loads of one item through a buffer resource over its 16 rows (the item
+// index is wave-uniform): row i is the scalar offset i * 2C, the lane's
+// column offset the one vector offset.  Lanes past the last column get an
+// offset beyond the resource and read zeros.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void amax_rht_load(const uint16_t* __restrict__ x, int64_t C, int64_t ncg,
+                                              int64_t item, int lane, uint2 (&v)[16]) {
+  const int64_t rb = item / ncg, cg = item - rb * ncg;
+  const uint32_t rowb = (uint32_t)C * 2u;
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + rb * 16 * C), (short)0, (int)(16u * rowb), kBufRsrcWord3);
+  const int64_t c0 = cg * 256 + lane * 4;
+  const int voff = c0 < C ? (int)(c0 * 2) : (int)0x7FFFFFF0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    v[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(i * rowb), 0));
+}
+
+__global__ __launch_bounds__(256) void k_amax_tile_rht(const uint16_t* __restrict__ x, int64_t R,
+                                                       int64_t C, uint32_t signs, float* amax_row,
+                                                       float* amax_col) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ncg = (C + 255) / 256, nitems = ncg * (R / 16);
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  int64_t it = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  ushort2v mr = {0, 0};
+  float mc = 0.0f;
+  uint2 a[16], b[16];
+  if (it < nitems) amax_rht_load(x, C, ncg, it, lane, a);
+  while (it < nitems) {
+    if (it + nw < nitems) amax_rht_load(x, C, ncg, it + nw, lane, b);
+    amax_rht_item(a, signs, mr, mc);
+    it += nw;
+    if (it >= nitems) break;
+    if (it + nw < nitems) amax_rht_load(x, C, ncg, it + nw, lane, a);
+    amax_rht_item(b, signs, mr, mc);
+    it += nw;
+  }
+  const uint32_t m = max((uint32_t)mr.x, (uint32_t)mr.y) << 16;
+  block_max_atomic(m, amax_row, nullptr);
+  block_max_atomic(f2u(mc * 0.25f), amax_col, nullptr);
 }
 
 // ---------------------------------------------------------------- rowwise encoder
@@ -613,13 +677,12 @@ hipError_t launch_amax_flat(const void* x, int64_t nchunk, bool rht, uint32_t si
 
 hipError_t launch_amax_tile_rht(const void* x, int64_t R, int64_t C, uint32_t signs,
                                 float* amax_row, float* amax_col, hipStream_t s) {
-  const int64_t lanes = C / 8;
-  const int gx = (int)((lanes + 255) / 256);
-  const int64_t nrb = R / 16;
-  const int rbs = pick_rbs(nrb, (lanes + 63) / 64);
-  const int64_t gy = (nrb + rbs - 1) / rbs;
-  hipLaunchKernelGGL(k_amax_tile_rht, dim3((unsigned)(gx * gy)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), R, C, gx, rbs, signs, amax_row, amax_col);
+  if (C * 32 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // 16 rows per buffer resource
+  const int64_t nitems = ((C + 255) / 256) * (R / 16);
+  int64_t g = (nitems + 3) / 4;
+  g = g < 1 ? 1 : (g > kAmaxRhtBlocks ? kAmaxRhtBlocks : g);
+  hipLaunchKernelGGL(k_amax_tile_rht, dim3((unsigned)g), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), R, C, signs, amax_row, amax_col);
   return hipGetLastError();
 }
 
