@@ -143,9 +143,9 @@ __device__ __forceinline__ float exp2_neg(int e) {
 }
 
 // ---------------------------------------------------------------- RHT
-// y <- 0.25 * H16 * D * y on 16 values held in one thread (natural-order
-// Sylvester H16; bit i of signs negates element i first).
-__device__ __forceinline__ void rht16(float (&y)[16], uint32_t signs) {
+// y <- H16 * D * y on 16 values held in one thread (natural-order Sylvester
+// H16; bit i of signs negates element i first), without the 1/4.
+__device__ __forceinline__ void rht16_unscaled(float (&y)[16], uint32_t signs) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) y[i] = u2f(f2u(y[i]) ^ (((signs >> i) & 1u) << 31));
 #pragma unroll
@@ -159,6 +159,11 @@ __device__ __forceinline__ void rht16(float (&y)[16], uint32_t signs) {
       }
     }
   }
+}
+
+// y <- 0.25 * H16 * D * y.
+__device__ __forceinline__ void rht16(float (&y)[16], uint32_t signs) {
+  rht16_unscaled(y, signs);
 #pragma unroll
   for (int i = 0; i < 16; ++i) y[i] = y[i] * 0.25f;
 }
@@ -229,21 +234,21 @@ __device__ __forceinline__ R16x8 sr_words(uint64_t grp, uint64_t seed, uint32_t 
 // (measured on 2^21 random inputs against that formula, no mismatch).  With
 // R = (65535 - r16) << 6 the carry happens iff r16 < floor(frac * 2^16), which
 // is the rule above bit for bit.  The two halves of a pair would share most of
-// R's bits, so each element gets a call of its own with +0 in the other slot
-// (+0 encodes to 0 for every R).  Only byte 0 of each result is defined here
-// (the instruction leaves the other bytes of its destination unspecified), so
-// the four pair bytes are gathered with byte permutes.
+// R's bits, so each pair is converted twice, once with the even element's R
+// and once with the odd element's, and the low nibble of the first result is
+// merged with the high nibble of the second.  Only byte 0 of each result is
+// defined here (the instruction leaves the other bytes of its destination
+// unspecified), so the four pair bytes are gathered with byte permutes.
 __device__ __forceinline__ uint32_t fp4x8_sr(const float (&v)[8], const R16x8& rnd) {
   typedef float f2 __attribute__((ext_vector_type(2)));
   uint32_t b[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t nw = ~rnd.w[k];                       // 65535 - r16 in both halves
-    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(
-        0u, f2{v[2 * k], 0.0f}, nw << 16, 1.0f, 0);      // R = (65535 - r16_even) << 6
-    const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(
-        0u, f2{0.0f, v[2 * k + 1]}, (nw >> 1) & 0x7FFF8000u, 1.0f, 0);  // odd, bits 30..15
-    b[k] = lo | hi;
+    const f2 pr = {v[2 * k], v[2 * k + 1]};
+    const uint32_t e = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pr, nw << 16, 1.0f, 0);
+    const uint32_t o = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pr, (nw >> 1) & 0x7FFF8000u, 1.0f, 0);
+    b[k] = (e & 0x0Fu) | (o & 0xF0u);                    // even from e (R bits 31..10), odd from o (30..9)
   }
   const uint32_t b01 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
   const uint32_t b23 = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);

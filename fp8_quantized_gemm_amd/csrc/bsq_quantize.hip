@@ -496,6 +496,19 @@ __device__ __forceinline__ void qt_tile_of_block(int pid, int tiles_r, int tiles
   tc = idx % tiles_c;
 }
 
+// max |x| over a thread's 16 rows x 8 BF16 values, as FP32 bits: the
+// magnitudes are compared as packed 16-bit integers, without unpacking.
+__device__ __forceinline__ uint32_t amax16x8_bits(const uint4 (&v)[16]) {
+  ushort2v m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, w[d] & 0x7FFF7FFFu));
+  }
+  return max((uint32_t)m.x, (uint32_t)m.y) << 16;
+}
+
 template <bool SR, bool RHT, bool TWO_D>
 __global__ __launch_bounds__(kQtThreads) void k_qt_nvfp4(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int tiles_r, int tiles_c, int do_row,
@@ -526,14 +539,7 @@ __global__ __launch_bounds__(kQtThreads) void k_qt_nvfp4(
 
   BlockScale tile{};
   if (TWO_D) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float y[8];
-      unpack8(v[i], y);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
-    }
+    uint32_t m = amax16x8_bits(v);
     m = max(m, dpp_xor1(m));
     tile.code = nvfp4_scale_code(u2f(m), do_row ? s_enc_row : s_enc_col);
     tile.enc = do_row ? enc_row[tile.code] : enc_col[tile.code];
@@ -575,12 +581,29 @@ __global__ __launch_bounds__(kQtThreads) void k_qt_nvfp4(
       float y[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) y[i] = tile_elem(v[i], j);
-      if (RHT) rht16(y, signs);
       uint32_t scode;
       float mult;
       if (TWO_D) {
         scode = tile.code;
         mult = tile.enc;
+      } else if (RHT) {
+        // The transform is taken without its 1/4.  The block amax of the
+        // transformed values is then 1/4 of this one exactly (all values are
+        // multiples of 2^-133), and y/4 * enc equals y * (enc/4), the same
+        // single rounding, whenever enc/4 is exact (enc >= 2^-124); smaller
+        // factors (amax near the top of the FP32 range) take the 1/4 on y.
+        rht16_unscaled(y, signs);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) m = fmaxf(m, fmaxf(fabsf(y[i]), fabsf(y[i + 1])));
+        scode = nvfp4_scale_code(m * 0.25f, s_enc_col);
+        mult = enc_col[scode];
+        if (mult < 0x1p-124f) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) y[i] = y[i] * 0.25f;
+        } else {
+          mult = mult * 0.25f;
+        }
       } else {
         uint32_t m = 0;
 #pragma unroll
