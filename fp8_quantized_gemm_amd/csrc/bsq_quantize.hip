@@ -129,7 +129,6 @@ __global__ void k_copy_amax(const float* src, float* dst) {
 
 // ---------------------------------------------------------------- amax passes
 
-constexpr int kAmaxPer = 8;         // chunks per thread per trip (amax pass)
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
 // no swizzle): out-of-range loads return zero.
 constexpr int kBufRsrcWord3 = 0x00020000;
@@ -137,40 +136,69 @@ constexpr int kBufRsrcWord3 = 0x00020000;
 #define BSQ_AMAX_RHT_BLOCKS 768
 #endif
 constexpr int kAmaxRhtBlocks = BSQ_AMAX_RHT_BLOCKS;   // workgroups of the RHT amax pass (3 per CU)
+constexpr int kAmaxFlatBlocks = 1024;                  // workgroups of the flat amax pass (4 per CU)
 
-// Grid-stride amax: each trip a thread loads kAmaxPer 16-byte chunks (a wave
-// reads kAmaxPer runs of 1 KiB) before reducing them; at most 2048 workgroups,
-// so the closing per-workgroup atomics stay few.
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+// Flat amax over a contiguous tensor of nchunk 16-byte chunks (8 BF16 values).
+// A work item is 512 consecutive chunks (8 KiB), one per wave: lane l loads
+// chunks 64 k + l (k = 0..7), so every load instruction covers 1 KiB.  Waves
+// walk the items grid-stride with the next item's loads in flight.  Without
+// RHT the magnitudes are compared as packed 16-bit integers; with RHT each
+// aligned 16-chunk (a lane pair) is transformed first.
+template <bool RHT>
+__device__ __forceinline__ void amax_flat_load(const uint4* __restrict__ x, int64_t nchunk,
+                                               int64_t item, int lane, uint4 (&v)[8]) {
+  const int64_t c0 = item * 512;
+  const int64_t left = nchunk - c0;
+  const int nrec = (int)(left >= 512 ? 512 * 16 : left * 16);
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(x + c0), (short)0, nrec,
+                                                                kBufRsrcWord3);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, k * 1024, 0));
+}
+
+template <bool RHT>
+__device__ __forceinline__ void amax_flat_item(const uint4 (&v)[8], int lane, uint32_t signs,
+                                               ushort2v& m16, uint32_t& m32) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (!RHT) {
+      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, w[d] & 0x7FFF7FFFu));
+    } else {
+      float y[8];
+      unpack8(v[k], y);
+      rht16_pair(y, lane & 1, signs);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m32 = max(m32, absbits(y[e]));
+    }
+  }
+}
+
 template <bool RHT>
 __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, int64_t nchunk,
                                                    uint32_t signs, float* a0, float* a1) {
-  const int t = threadIdx.x, lane = t & 63;
-  uint32_t m = 0;
-  for (int64_t base = (int64_t)blockIdx.x * 256 * kAmaxPer; base < nchunk;
-       base += (int64_t)gridDim.x * 256 * kAmaxPer) {
-    uint4 v[kAmaxPer];
-#pragma unroll
-    for (int k = 0; k < kAmaxPer; ++k) {
-      const int64_t q = base + k * 256 + t;
-      v[k] = q < nchunk ? x[q] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < kAmaxPer; ++k) {
-      if (!RHT) {
-        // BF16 magnitudes compare as unsigned 15-bit integers; the widening to
-        // FP32 bits (<< 16) keeps the order
-        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = max(m, max((w[i] & 0x7FFFu) << 16, w[i] & 0x7FFF0000u));
-      } else {
-        float y[8];
-        unpack8(v[k], y);
-        rht16_pair(y, lane & 1, signs);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m = max(m, absbits(y[e]));
-      }
-    }
+  const int lane = threadIdx.x & 63;
+  const int64_t nitems = (nchunk + 511) / 512;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  int64_t it = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  ushort2v m16 = {0, 0};
+  uint32_t m32 = 0;
+  uint4 a[8], b[8];
+  if (it < nitems) amax_flat_load<RHT>(x, nchunk, it, lane, a);
+  while (it < nitems) {
+    if (it + nw < nitems) amax_flat_load<RHT>(x, nchunk, it + nw, lane, b);
+    amax_flat_item<RHT>(a, lane, signs, m16, m32);
+    it += nw;
+    if (it >= nitems) break;
+    if (it + nw < nitems) amax_flat_load<RHT>(x, nchunk, it + nw, lane, a);
+    amax_flat_item<RHT>(b, lane, signs, m16, m32);
+    it += nw;
   }
+  const uint32_t m = RHT ? m32 : max((uint32_t)m16.x, (uint32_t)m16.y) << 16;
   block_max_atomic(m, a0, a1);
 }
 
@@ -183,8 +211,6 @@ __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, 
 //    packed BF16 pairs (sign-bit flips) and the 1/4 applied to the final max
 //    (exact: inputs are multiples of 2^-133, so every transformed value is,
 //    and scaling by 1/4 stays in the FP32 range without rounding).
-typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ void amax_rht_item(const uint2 (&v)[16], uint32_t signs, ushort2v& mr,
                                               float& mc) {
 #pragma unroll
@@ -687,8 +713,9 @@ hipError_t launch_copy_amax(const float* src, float* dst, hipStream_t s) {
 
 hipError_t launch_amax_flat(const void* x, int64_t nchunk, bool rht, uint32_t signs, float* a0,
                             float* a1, hipStream_t s) {
-  int64_t g = (nchunk + 256 * kAmaxPer - 1) / (256 * kAmaxPer);
-  g = g < 1 ? 1 : (g > 2048 ? 2048 : g);
+  const int64_t nitems = (nchunk + 511) / 512;
+  int64_t g = (nitems + 3) / 4;
+  g = g < 1 ? 1 : (g > kAmaxFlatBlocks ? kAmaxFlatBlocks : g);
   const dim3 grid((unsigned)g), block(256);
   const uint4* xp = static_cast<const uint4*>(x);
   if (rht)
