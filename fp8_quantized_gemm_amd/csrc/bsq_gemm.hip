@@ -11,10 +11,12 @@
 // Tiling: 256 x 256 output tile per 512-thread workgroup (8 waves as 2 x 4,
 // each 128 (M) x 64 (N) = 4 x 2 MFMA tiles of 32 x 32); each wave computes
 // D = B_tile . A_tile^T so that every lane holds consecutive output columns.
-//  * k_gemm_mx (K % 128 == 0, aligned operands): 64 code bytes per row per
+//  * k_gemm_mx (K % 512 == 0, aligned operands): 64 code bytes per row per
 //    stage (K 64 for MXFP8, 128 for MXFP4) staged in LDS by global -> LDS
-//    direct loads three stages ahead (four stage buffers), one barrier per
-//    stage.
+//    direct loads four stages ahead (four stage buffers), scales 16 bytes per
+//    row per period of 8 / 4 stages, one barrier per stage; each wave reads the
+//    next stage's fragments into a second register set while the MFMAs of the
+//    current stage run.
 //  * k_gemm (any K): the general path, register-staged, one stage ahead.
 //
 // K order inside a stage: an MFMA only needs A and B to agree on which K index
@@ -290,20 +292,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
 
 // ---------------------------------------------------------------- staged kernel
 //
-// Stage layout in LDS (34 KiB, four buffers): A codes 256 rows x 64 bytes, B
-// codes the same (16-byte chunk c of row r in slot c ^ ((r >> 2) & 3), which
-// keeps the fragment reads of 16 consecutive rows on distinct banks), then one
-// scale dword per row of A and of B (MXFP8: the dword holding this stage's two
-// scales and the next stage's; MXFP4: this stage's four).  Wave w stages rows
-// 32 w .. 32 w + 31 of both operands' codes (4 direct loads of 16 rows x 64
-// bytes) and the scale dwords of 64 rows of one operand (1 direct load).
+// Stage layout in LDS: four code buffers of 32 KiB (A codes 256 rows x 64
+// bytes, then B codes; 16-byte chunk c of row r in slot c ^ ((r >> 2) & 3),
+// which keeps the fragment reads of 16 consecutive rows on distinct banks),
+// then two scale buffers of 8 KiB (16 scale bytes of each of the 256 A rows
+// and 256 B rows: four MXFP4 stages or eight MXFP8 stages).  Wave w stages rows
+// 32 w .. 32 w + 31 of both operands' codes every stage (4 direct loads of 16
+// rows x 64 bytes) and 64 rows of one operand's scales once per scale period
+// (one direct load of 64 rows x 16 bytes).  The kernel is bound by the number
+// of L2 requests, not bytes: a row's scales are fetched as one 16-byte piece
+// per period instead of one dword per stage, which removes over a third of the
+// requests.
 constexpr int kMxRowB = 64;
 constexpr int kMxCodeB = 256 * kMxRowB;
-constexpr int kMxStageB = 2 * kMxCodeB + 2 * 256 * 4;
+constexpr int kMxStageB = 2 * kMxCodeB;                  // 32 KiB of codes per stage
 constexpr int kMxStages = 4;
-constexpr int kMxLds = kMxStages * kMxStageB > kEpiLds ? kMxStages * kMxStageB : kEpiLds;
-constexpr int kMxDma = 5;                                // direct loads per wave per stage
+constexpr int kMxScOff = kMxStages * kMxStageB;          // scale buffers after the code buffers
+constexpr int kMxScB = 2 * 256 * 16;                     // one scale period, both operands
+constexpr int kMxLds = kMxScOff + 2 * kMxScB > kEpiLds ? kMxScOff + 2 * kMxScB : kEpiLds;
+constexpr int kMxDma = 4;                                // code loads per wave per stage
 static_assert(kMxLds <= 160 * 1024, "MX staged LDS plan");
+
+// Stages per scale period: 16 bytes of a row hold 4 MXFP4 stages (128 K
+// each, 4 blocks) or 8 MXFP8 stages (64 K each, 2 blocks).
+template <int FMT>
+constexpr int mx_period() { return FMT == kMXFP8 ? 8 : 4; }
 
 struct MxLoadMap {
   uint32_t code[4];                                      // byte offset of this lane's 16 bytes
@@ -311,81 +324,174 @@ struct MxLoadMap {
 };
 
 template <int FMT>
-__device__ __forceinline__ void mx_stage(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
-                                         const uint8_t* bs, const MxLoadMap& lm, int64_t kt,
-                                         uint32_t st, int w) {
-  const int64_t sdw = FMT == kMXFP8 ? (kt >> 1) : kt;     // scale dword index along the row
+__device__ __forceinline__ void mx_stage(const uint8_t* ac, const uint8_t* bc, const MxLoadMap& lm,
+                                         int64_t kt, uint32_t st, int w) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* base = (i < 2 ? ac : bc) + kt * kMxRowB;
     dma_to_lds<16>(base, lm.code[i], st + (i >> 1) * kMxCodeB + (w * 32 + (i & 1) * 16) * kMxRowB);
   }
-  dma_to_lds<4>((w < 4 ? as : bs) + sdw * 4, lm.scale, st + 2 * kMxCodeB + (w >> 2) * 1024 + (w & 3) * 256);
 }
 
-// One stage of MFMAs from LDS buffer `buf`; P = stage parity (MXFP8 scale byte).
-template <int FMT, int P>
-__device__ __forceinline__ void mx_compute(floatx16 (&acc)[4][2], const uint8_t* buf, int wm,
-                                           int wn, int h, int l32) {
-  constexpr int FMTC = FMT == kMXFP8 ? 0 : 4;            // cbsz / blgp operand type
+// Scale period q (16 bytes per row) into scale buffer `sb`.
+__device__ __forceinline__ void mx_stage_scales(const uint8_t* as, const uint8_t* bs,
+                                                const MxLoadMap& lm, int64_t q, uint32_t sb, int w) {
+  dma_to_lds<16>((w < 4 ? as : bs) + q * 16, lm.scale, sb + (w >> 2) * (256 * 16) + (w & 3) * (64 * 16));
+}
+
+// Fragments and scale operands of one stage for one wave.  MXFP8: fa[0]/fa[1]
+// are bytes 0-15 / 16-31 of the operand (chunks h and 2 + h); MXFP4: fa[s] is
+// the operand of K step s (chunk 2h + s, upper half zero).  Scale operands are
+// read as the byte (MXFP8) or byte pair (MXFP4, the K step selecting one) the
+// instruction uses: lane half h carries block h of the instruction (MXFP8) or
+// blocks 2h, 2h + 1 of the stage (MXFP4).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct MxFrag {
+  u32x4 fa[2][4], fb[2][2];
+  uint32_t sa[4], sb[2];
+};
+
+// Read number Q (0..17) of a stage's fragments: 8 A chunks, 4 B chunks, 4 A
+// scales, 2 B scales.  sb0 = the stage's first scale byte within its period's
+// 16 bytes (MXFP8: 2 x position, 2 blocks per stage; MXFP4: 4 x position).
+template <int FMT, int Q>
+__device__ __forceinline__ void mx_read(MxFrag& F, const uint8_t* buf, const uint8_t* sbuf, int sb0,
+                                        int wm, int wn, int h, int l32) {
   const uint8_t* La = buf;
   const uint8_t* Lb = buf + kMxCodeB;
-  const uint8_t* Sa = buf + 2 * kMxCodeB;
-  const uint8_t* Sb = Sa + 1024;
-  // scale operands: MXFP8 lane half h carries the scale of the instruction's
-  // block h (stage block h, byte 2P + h); MXFP4 lane half h supplies stage
-  // blocks 2h + s (byte 2h + s), selected below by the K step s
-  uint32_t sca[4], scb[2];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-    sca[mi] = *reinterpret_cast<const uint32_t*>(Sa + (wm * 128 + mi * 32 + l32) * 4) >> (FMT == kMXFP8 ? 8 * h : 16 * h);
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni)
-    scb[ni] = *reinterpret_cast<const uint32_t*>(Sb + (wn * 64 + ni * 32 + l32) * 4) >> (FMT == kMXFP8 ? 8 * h : 16 * h);
+  const uint8_t* Sa = sbuf;
+  const uint8_t* Sb = sbuf + 256 * 16;
   const auto chunk = [](const uint8_t* base, int row, int c) {
-    return *reinterpret_cast<const uint4*>(base + row * kMxRowB + ((c ^ ((row >> 2) & 3)) << 4));
+    return *reinterpret_cast<const u32x4*>(base + row * kMxRowB + ((c ^ ((row >> 2) & 3)) << 4));
   };
-  constexpr int STEPS = FMT == kMXFP8 ? 1 : 2;
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    intx8 fa[4], fb[2];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int row = wm * 128 + mi * 32 + l32;
-      // MXFP8: bytes 0-15 = elements [16h, 16h + 16) of block 0 (chunk h),
-      // bytes 16-31 = the same of block 1 (chunk 2 + h); MXFP4: block 2h + s
-      const uint4 lo = chunk(La, row, FMT == kMXFP8 ? h : 2 * h + s);
-      const uint4 hi = FMT == kMXFP8 ? chunk(La, row, 2 + h) : make_uint4(0, 0, 0, 0);
-      fa[mi] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int row = wn * 64 + ni * 32 + l32;
-      const uint4 lo = chunk(Lb, row, FMT == kMXFP8 ? h : 2 * h + s);
-      const uint4 hi = FMT == kMXFP8 ? chunk(Lb, row, 2 + h) : make_uint4(0, 0, 0, 0);
-      fb[ni] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    constexpr int SEL = FMT == kMXFP8 ? 2 * P : 0;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        acc[mi][ni] = mfma_mx<FMTC>(FMT == kMXFP8 ? SEL : s, fb[ni], fa[mi], acc[mi][ni], scb[ni], sca[mi]);
+  if (Q < 8) {
+    const int j = Q >> 2, mi = Q & 3, row = wm * 128 + mi * 32 + l32;
+    F.fa[j][mi] = chunk(La, row, FMT == kMXFP8 ? (j == 0 ? h : 2 + h) : 2 * h + j);
+  } else if (Q < 12) {
+    const int j = (Q - 8) >> 1, ni = (Q - 8) & 1, row = wn * 64 + ni * 32 + l32;
+    F.fb[j][ni] = chunk(Lb, row, FMT == kMXFP8 ? (j == 0 ? h : 2 + h) : 2 * h + j);
+  } else if (Q < 16) {
+    const int mi = Q - 12, row = wm * 128 + mi * 32 + l32;
+    F.sa[mi] = FMT == kMXFP8 ? (uint32_t)Sa[row * 16 + sb0 + h]
+                             : (uint32_t)*reinterpret_cast<const uint16_t*>(Sa + row * 16 + sb0 + 2 * h);
+  } else {
+    const int ni = Q - 16, row = wn * 64 + ni * 32 + l32;
+    F.sb[ni] = FMT == kMXFP8 ? (uint32_t)Sb[row * 16 + sb0 + h]
+                             : (uint32_t)*reinterpret_cast<const uint16_t*>(Sb + row * 16 + sb0 + 2 * h);
   }
 }
 
-// One stage: wait for it, barrier, stage kt + 3, compute kt.  P = kt & 1
-// (only MXFP8 uses it, to pick the scale bytes of its half of the dword).
+// MFMA number I of a stage (MXFP8: 8, mi = I / 2, ni = I % 2; MXFP4: 16, K step
+// I / 8).
+template <int FMT, int I>
+__device__ __forceinline__ void mx_mfma(floatx16 (&acc)[4][2], const MxFrag& F) {
+  constexpr int FMTC = FMT == kMXFP8 ? 0 : 4;            // cbsz / blgp operand type
+  constexpr int s = FMT == kMXFP8 ? 0 : I >> 3;
+  constexpr int mi = (I & 7) >> 1, ni = I & 1;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const u32x4 al = F.fa[s][mi], bl = F.fb[s][ni];
+  const u32x4 ah = FMT == kMXFP8 ? F.fa[1][mi] : z;
+  const u32x4 bh = FMT == kMXFP8 ? F.fb[1][ni] : z;
+  const intx8 a = __builtin_bit_cast(intx8, __builtin_shufflevector(al, ah, 0, 1, 2, 3, 4, 5, 6, 7));
+  const intx8 b = __builtin_bit_cast(intx8, __builtin_shufflevector(bl, bh, 0, 1, 2, 3, 4, 5, 6, 7));
+  acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[mi][ni], FMTC, FMTC, s,
+                                                                (int)F.sb[ni], s, (int)F.sa[mi]);
+}
+
+// Reads issued after MFMA I: [lo(I), lo(I + 1)), spread over the first 8 MFMAs
+// (MXFP8) or the first 12 (MXFP4) so that they complete before the barrier.
+template <int FMT>
+__host__ __device__ constexpr int mx_rd_lo(int i) {
+  return FMT == kMXFP8 ? (i * 18 + 7) / 8 > 18 ? 18 : (i * 18 + 7) / 8
+                       : (i * 18 + 11) / 12 > 18 ? 18 : (i * 18 + 11) / 12;
+}
+
+template <int FMT, int I>
+__device__ __forceinline__ void mx_step(floatx16 (&acc)[4][2], const MxFrag& C, MxFrag& N,
+                                        const uint8_t* nbuf, const uint8_t* nsbuf, int nsb0, int wm,
+                                        int wn, int h, int l32) {
+  mx_mfma<FMT, I>(acc, C);
+  constexpr int lo = mx_rd_lo<FMT>(I), hi = mx_rd_lo<FMT>(I + 1);
+  if (lo + 0 < hi) mx_read<FMT, lo + 0 < 18 ? lo + 0 : 17>(N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  if (lo + 1 < hi) mx_read<FMT, lo + 1 < 18 ? lo + 1 : 17>(N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  if (lo + 2 < hi) mx_read<FMT, lo + 2 < 18 ? lo + 2 : 17>(N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Everything a stage needs besides the fragments (wave-uniform).
+struct MxCtx {
+  const uint8_t* ac;
+  const uint8_t* as;
+  const uint8_t* bc;
+  const uint8_t* bs;
+  uint8_t* smem;
+  uint32_t smem_lds;
+  int64_t KT, NP;            // stages, scale periods
+  int w;
+};
+
+// Scale slot of stage kt (one direct load every stage, so that this wave's
+// load count per stage is fixed): at a period start (kt % period == 0) the
+// scales of period q + 1 into its buffer; otherwise lane 0 reloads its own 16
+// bytes of the current period into the place they already occupy (one L2
+// request, same bytes).
+__device__ __forceinline__ void mx_scale_slot(const MxCtx& x, const MxLoadMap& lm, int64_t q,
+                                              int64_t ph, int lane) {
+  if (ph == 0) {
+    const int64_t nq = q + 1 < x.NP ? q + 1 : x.NP - 1;
+    mx_stage_scales(x.as, x.bs, lm, nq, x.smem_lds + kMxScOff + (uint32_t)((q + 1) & 1) * kMxScB, x.w);
+  } else if (lane == 0) {
+    mx_stage_scales(x.as, x.bs, lm, q, x.smem_lds + kMxScOff + (uint32_t)(q & 1) * kMxScB, x.w);
+  }
+}
+
+// Stage kt (P = kt & 1): wait until stage kt + 1 has landed (this wave's loads,
+// then everyone's), the scale slot, stage kt + 4 into the buffer of stage kt
+// (whose fragments are in registers), then the MFMAs of kt on C with the
+// fragment reads of kt + 1 into N interleaved.  This wave's loads issued after
+// stage kt + 1's are the scale slots and stages of kt + 2 and kt + 3, so at
+// most 2 (1 + kMxDma) may remain.  A period's scales are issued before the
+// code stage four ahead, which is waited for before that period's first read.
 template <int FMT, int P>
-__device__ __forceinline__ void mx_iter(floatx16 (&acc)[4][2], uint8_t* smem, uint32_t smem_lds,
-                                        const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
-                                        const uint8_t* bs, const MxLoadMap& lm, int64_t kt,
-                                        int64_t KT, int w, int wm, int wn, int h, int l32) {
-  wait_vmcnt<2 * kMxDma>();                    // this wave's loads of stage kt are in
-  lds_barrier();                               // everyone's are; stage kt - 1 is read
-  const int64_t nk = kt + 3 < KT ? kt + 3 : KT - 1;
-  mx_stage<FMT>(ac, as, bc, bs, lm, nk, smem_lds + (uint32_t)((kt + 3) & 3) * kMxStageB, w);
-  mx_compute<FMT, P>(acc, smem + (kt & 3) * kMxStageB, wm, wn, h, l32);
+__device__ __forceinline__ void mx_iter(floatx16 (&acc)[4][2], MxFrag& C, MxFrag& N,
+                                        const MxCtx& x, const MxLoadMap& lm, int64_t kt, int wm,
+                                        int wn, int h, int l32, int lane) {
+  constexpr int PER = mx_period<FMT>();
+  wait_vmcnt<2 * (1 + kMxDma)>();
+  lds_barrier();                               // everyone's; all fragments of kt are in registers
+  const int64_t q = kt / PER, ph = kt - q * PER;
+  mx_scale_slot(x, lm, q, ph, lane);
+  const int64_t nk = kt + 4 < x.KT ? kt + 4 : x.KT - 1;
+  mx_stage<FMT>(x.ac, x.bc, lm, nk, x.smem_lds + (uint32_t)(kt & 3) * kMxStageB, x.w);
+  const uint8_t* nbuf = x.smem + ((kt + 1) & 3) * kMxStageB;
+  const int64_t nq = (kt + 1) / PER;
+  const uint8_t* nsbuf = x.smem + kMxScOff + (nq & 1) * kMxScB;
+  const int nsb0 = (int)(kt + 1 - nq * PER) * (FMT == kMXFP8 ? 2 : 4);
+  mx_step<FMT, 0>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  mx_step<FMT, 1>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  mx_step<FMT, 2>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  mx_step<FMT, 3>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  mx_step<FMT, 4>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  mx_step<FMT, 5>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  mx_step<FMT, 6>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  mx_step<FMT, 7>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  if (FMT == kMXFP4) {
+    mx_step<FMT, 8>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+    mx_step<FMT, 9>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+    mx_step<FMT, 10>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+    mx_step<FMT, 11>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+    mx_step<FMT, 12>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+    mx_step<FMT, 13>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+    mx_step<FMT, 14>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+    mx_step<FMT, 15>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
+  }
+}
+
+template <int FMT, int Q>
+__device__ __forceinline__ void mx_read_all(MxFrag& F, const uint8_t* buf, const uint8_t* sbuf,
+                                            int wm, int wn, int h, int l32) {
+  mx_read<FMT, Q>(F, buf, sbuf, 0, wm, wn, h, l32);
+  if constexpr (Q + 1 < 18) mx_read_all<FMT, Q + 1>(F, buf, sbuf, wm, wn, h, l32);
 }
 
 template <int FMT>
@@ -402,7 +508,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
   const int h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(wave);
   const int64_t code_ld = FMT == kMXFP8 ? K : K / 2, scale_ld = K / 32;
-  const int64_t KT = code_ld / kMxRowB;                  // stages
+  constexpr int P = mx_period<FMT>();
+  MxCtx x;
+  x.ac = a_codes;
+  x.as = a_scales;
+  x.bc = b_codes;
+  x.bs = b_scales;
+  x.smem = smem;
+  x.smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  x.KT = code_ld / kMxRowB;                              // stages (a multiple of the period)
+  x.NP = x.KT / P;
+  x.w = w;
   MxLoadMap lm;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -425,19 +541,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  // prologue: the scales of period 0 and the code stages 0..3, each stage
+  // preceded by a scale slot's worth of loads so the per-stage count is fixed
+  mx_stage_scales(a_scales, b_scales, lm, 0, x.smem_lds + kMxScOff, w);
 #pragma unroll
-  for (int k = 0; k < 3; ++k)
-    mx_stage<FMT>(a_codes, a_scales, b_codes, b_scales, lm, k < KT ? k : KT - 1,
-                  smem_lds + k * kMxStageB, w);
-  if (FMT == kMXFP8) {                         // KT is even (K % 128 == 0)
-    for (int64_t kt = 0; kt < KT; kt += 2) {
-      mx_iter<FMT, 0>(acc, smem, smem_lds, a_codes, a_scales, b_codes, b_scales, lm, kt, KT, w, wm, wn, h, l32);
-      mx_iter<FMT, 1>(acc, smem, smem_lds, a_codes, a_scales, b_codes, b_scales, lm, kt + 1, KT, w, wm, wn, h, l32);
-    }
-  } else {
-    for (int64_t kt = 0; kt < KT; ++kt)
-      mx_iter<FMT, 0>(acc, smem, smem_lds, a_codes, a_scales, b_codes, b_scales, lm, kt, KT, w, wm, wn, h, l32);
+  for (int k = 0; k < 4; ++k) {
+    if (k > 0 && lane == 0) mx_stage_scales(a_scales, b_scales, lm, 0, x.smem_lds + kMxScOff, w);
+    mx_stage<FMT>(a_codes, b_codes, lm, k < x.KT ? k : x.KT - 1, x.smem_lds + k * kMxStageB, w);
+  }
+  wait_vmcnt<3 * (1 + kMxDma)>();              // period-0 scales and stage 0 in
+  lds_barrier();
+  MxFrag F0, F1;
+  mx_read_all<FMT, 0>(F0, smem, smem + kMxScOff, wm, wn, h, l32);
+  for (int64_t kt = 0; kt < x.KT; kt += 2) {   // KT is even (a multiple of the period)
+    mx_iter<FMT, 0>(acc, F0, F1, x, lm, kt, wm, wn, h, l32, lane);
+    mx_iter<FMT, 1>(acc, F1, F0, x, lm, kt + 1, wm, wn, h, l32, lane);
   }
   wait_vmcnt<0>();                             // the clamped tail loads land in LDS the epilogue reuses
   lds_barrier();
@@ -469,10 +587,10 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   }
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
   uint16_t* cp = static_cast<uint16_t*>(c);
-  // staged kernel: whole 64-byte code segments and aligned scale dwords per
-  // stage, 32-bit byte offsets within each operand
-  const bool staged = K > 0 && K % 128 == 0 && al16(ac) && al16(bc) &&
-                      ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(bs)) % 4 == 0) &&
+  // staged kernel: whole 64-byte code segments per stage, 16-byte scale pieces
+  // per scale period (K % 512 == 0 for both formats), 32-bit byte offsets
+  // within each operand
+  const bool staged = K > 0 && K % 512 == 0 && al16(ac) && al16(bc) && al16(as) && al16(bs) &&
                       M * code_ld < ((int64_t)1 << 32) && N * code_ld < ((int64_t)1 << 32);
   static bool mx_attr_set = false;
   if (staged) {
