@@ -326,7 +326,7 @@ def main():
                    "ffn": step.dims["ffn"], "rht": not args.no_rht,
                    "step_tflop": round(step.flops / 1e12, 3),
                    "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "bsq k_gemm<NVFP4> (6 launches per step)",
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_nvfp4_pp (NVFP4 GEMM, 6 launches per step)",
                      "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": gemm_traffic(args.workload),
