@@ -221,7 +221,7 @@ def cpu_baseline(workload, rht):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         blas_threads = os.cpu_count() or 1
-    TOK, NOUT = 8192, 28672                   # about 12 s on the 16 host cores of an MI355X node
+    TOK, NOUT = 8192, 28672                   # about 12 s with 16 host cores
     X = synth.workload_tensor(workload, "X", "cpu")
     W = synth.workload_tensor(workload, "W_gu", "cpu")
     bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
