@@ -275,15 +275,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t n = n0 + wn * 64 + ni * 32 + 8 * q + 4 * h;
-        uint32_t b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(acc[mi][ni][4 * q + e] * alpha);
+        const floatx16& a = acc[mi][ni];
+        const uint32_t w0 = pack_bf16x2(a[4 * q] * alpha, a[4 * q + 1] * alpha);
+        const uint32_t w1 = pack_bf16x2(a[4 * q + 2] * alpha, a[4 * q + 3] * alpha);
         if (vec_store && n + 3 < N) {
-          *reinterpret_cast<uint2*>(crow + n) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+          *reinterpret_cast<uint2*>(crow + n) = make_uint2(w0, w1);
         } else {
+          const uint16_t b[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1, (uint16_t)(w1 >> 16)};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (n + e < N) crow[n + e] = (uint16_t)b[e];
+            if (n + e < N) crow[n + e] = b[e];
         }
       }
     }

@@ -11,10 +11,13 @@ typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;     // NaN stays NaN
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two FP32 values -> a packed BF16 pair (lo in bits 0-15), rounded to nearest
+// even by the hardware pack: the same bits as the integer rounding rule for
+// every non-NaN input, denormals and ties included; NaN stays NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // E4M3 byte SEL of w -> float (exact; OCP E4M3FN on gfx950).
@@ -79,7 +82,7 @@ __device__ __forceinline__ void tile_of_block(int pid, int tiles_m, int tiles_n,
 
 // Epilogue of a 512-thread, 256 x 256 tile whose 8 waves (2 x 4) each hold a
 // 128 x 64 accumulator as 4 x 2 MFMA tiles of 32 x 32 in the D = B . A^T
-// layout: alpha * acc -> BF16 RNE, staged per wave through LDS so that global
+// layout: alpha * acc -> BF16 (RNE), staged per wave through LDS so that global
 // stores are whole 128-byte row segments.  Lane holds output row
 // m = 32 mi + l32 and columns n = 32 ni + 8 q + 4 h + e (e = 0..3) of the wave
 // tile.  The caller has passed a barrier after the last LDS read of its main
@@ -98,11 +101,10 @@ __device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[4][2], uin
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint32_t b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(acc[mi][ni][4 * q + e] * alpha);
+        const floatx16& a = acc[mi][ni];
         *reinterpret_cast<uint2*>(E + (mi * 32 + l32) * kEpiRowB + (ni * 32 + q * 8 + h * 4) * 2) =
-            make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+            make_uint2(pack_bf16x2(a[4 * q] * alpha, a[4 * q + 1] * alpha),
+                       pack_bf16x2(a[4 * q + 2] * alpha, a[4 * q + 3] * alpha));
       }
   __syncthreads();
   const int64_t gm0 = m0 + wm * 128, gn = n0 + wn * 64 + (lane & 7) * 8;

@@ -126,6 +126,7 @@ def _special_bits(R, C, seed):
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], dtype=np.float32)
     b[4, :] = (np.resize(mids, C).view(np.uint32) >> 16).astype(np.uint16)
     b[5, :] = 0x0001                               # the smallest subnormal everywhere
+    b[16:32, :8] = 0                               # all-zero column blocks (scale 0, encode factor 0)
     return b
 
 
