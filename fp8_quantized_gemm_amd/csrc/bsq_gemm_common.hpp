@@ -116,7 +116,10 @@ __device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[4][2], uin
     const uint4 v = *reinterpret_cast<const uint4*>(E + row * kEpiRowB + (lane & 7) * 16);
     uint16_t* dst = c + gm * ldc + gn;
     if (vec_store && gn + 7 < N) {
-      *reinterpret_cast<uint4*>(dst) = v;
+      // streaming store: the output (GB-sized) is not kept in L2 / MALL, so
+      // the next kernel does not pay for writing it back
+      typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4n{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4n*>(dst));
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
