@@ -34,6 +34,14 @@ __device__ __forceinline__ halfx2 nvfp4_scale_pair(uint32_t w) {
   return __builtin_bit_cast(halfx2, __builtin_amdgcn_cvt_pkrtz(s, s));
 }
 
+// Block scales of E4M3 bytes 2H and 2H + 1 of w as the FP16 pair
+// {S0 * 2^7, S1 * 2^7} in one scaled convert (the scale operand contributes
+// its power of two; exact for the same reason).
+template <int H>
+__device__ __forceinline__ halfx2 nvfp4_scale_pairs2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 128.0f, H != 0);
+}
+
 // 8 E2M1 codes (nibble i = element i of one dword) times a block scale, as 8
 // FP16 values v * S * 2^-7 (exact), in element order.
 // gfx950's FP4 -> FP16 pair convert turns byte k of the dword (elements 2k and

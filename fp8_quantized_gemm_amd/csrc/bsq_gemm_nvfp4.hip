@@ -358,7 +358,7 @@ __device__ __forceinline__ uint32_t pp_pk_sel(uint32_t w, int sel, halfx2 s) {
 }
 
 // Pairs of the expansion issued after MFMA k of a slot: pairs [lo(k), lo(k+1)),
-// spread over MFMAs 2..13 (the scale pairs are formed after MFMAs 0 and 1).
+// spread over MFMAs 2..13 (the scale pairs are formed after MFMA 0).
 __host__ __device__ constexpr int pp_pk_lo(int k) {
   return k < 2 ? 0 : (((k - 2) * 16 + 11) / 12 > 16 ? 16 : ((k - 2) * 16 + 11) / 12);
 }
@@ -379,8 +379,11 @@ __device__ __forceinline__ void pp_mfma_slot(floatx16 (&acc)[4][2], const PpFrag
   for (int k = 0; k < 16; ++k) {
     const int st = k >> 3, mi = (k & 7) >> 1, ni = k & 1;
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[st][ni], f.a[st][mi], acc[mi][ni], 0, 0, 0);
-    if (k == 0) s0 = nvfp4_scale_pair<2 * Q>(raw.sw);
-    if (k == 1) s1 = nvfp4_scale_pair<2 * Q + 1>(raw.sw);
+    if (k == 0) {
+      const halfx2 ss = nvfp4_scale_pairs2<Q>(raw.sw);   // both block scales of the chunk
+      s0 = halfx2{ss.x, ss.x};
+      s1 = halfx2{ss.y, ss.y};
+    }
     const int lo = pp_pk_lo(k), hi = pp_pk_lo(k + 1);
 #pragma unroll
     for (int p = 0; p < 16; ++p)
