@@ -6,10 +6,13 @@
 // (ingredient 3), 16x16 weight tiles (ingredient 4), RNE / stochastic rounding
 // (ingredient 5).  HN page opcode84: MXFP4 / MXFP8 with E8M0 scales per 32.
 //
-// Memory layout and work split (all kernels are HBM-bound streams):
-//  * Every lane moves 16-byte chunks of 8 BF16 values and every global access
-//    instruction of a wave covers one contiguous run (1 KiB of input; codes
-//    and scales contiguous across lanes).
+// Memory layout and work split (all kernels are HBM-bound streams, the
+// stochastic-rounding encoders excepted: Philox makes them VALU-bound):
+//  * Lanes move 16-byte chunks of 8 BF16 values (8-byte chunks in the RHT
+//    amax pass) and every global access instruction of a wave covers one
+//    contiguous run per row (codes and scales contiguous across lanes).
+//  * Amax passes: each wave reduces grid-stride work items with the next
+//    item's loads in flight; one atomic max per workgroup at the end.
 //  * Rowwise: a 1x16 block is a lane pair, a 1x32 MX block a lane quad; the
 //    block amax is combined with quad_perm DPP moves, no LDS.
 //  * Row + column: a lane owns 8 columns x 16 (or 32) rows, so each column
@@ -132,10 +135,7 @@ __global__ void k_copy_amax(const float* src, float* dst) {
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
 // no swizzle): out-of-range loads return zero.
 constexpr int kBufRsrcWord3 = 0x00020000;
-#ifndef BSQ_AMAX_RHT_BLOCKS
-#define BSQ_AMAX_RHT_BLOCKS 768
-#endif
-constexpr int kAmaxRhtBlocks = BSQ_AMAX_RHT_BLOCKS;   // workgroups of the RHT amax pass (3 per CU)
+constexpr int kAmaxRhtBlocks = 768;                   // workgroups of the RHT amax pass (3 per CU)
 constexpr int kAmaxFlatBlocks = 1024;                  // workgroups of the flat amax pass (4 per CU)
 
 typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
