@@ -120,6 +120,8 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
   float* ar = do_row ? amax_row : nullptr;
   float* ac = do_col ? amax_col : nullptr;
   if (!x || !aligned16(x)) return BSQ_EINVAL;
+  // the column RHT amax pass addresses 16 rows (32 * cols bytes) per buffer resource
+  if (nv && rht_col && do_col && cols >= ((int64_t)1 << 26)) return BSQ_EINVAL;
 
   hipError_t e;
   if (nv) {

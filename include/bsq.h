@@ -125,7 +125,8 @@ bsq_status mx_quantize(const void* x, int64_t rows, int64_t cols, bsq_format fmt
  *   rnd        : RNE or SR (SR: rowwise stream 0, columnwise stream 1); not SR
  *                with 2D tiles or MXFP8.
  *   rht_col    : nonzero = RHT along rows (the blocked dim of x^T) for the col
- *                output only; NVFP4 1x16 only.
+ *                output only; NVFP4 1x16 only; with the col output it needs
+ *                cols < 2^26 (BSQ_EINVAL otherwise).
  *   amax_row / amax_col : out, device FP32 (NVFP4 only; ignored for MX).
  *                amax_row = max|x|; amax_col = max|RHT(x^T)| with rht_col,
  *                else equal to amax_row.

@@ -94,6 +94,7 @@ def test_quantize_transpose_argument_errors():
     assert _qt(block_rows=16, rnd=1) == bsq.BSQ_EUNSUPPORTED
     assert _qt(block_rows=16, rht=1) == bsq.BSQ_EUNSUPPORTED
     assert _qt(x=None) == bsq.BSQ_EINVAL
+    assert _qt(cols=1 << 26, rht=1) == bsq.BSQ_EINVAL     # column RHT amax addressing limit
     L = bsq.lib()
     # partial triple: codes given, scales missing
     assert L.quantize_transpose(FAKE, 32, 32, 0, 1, 0, 0, 0, 0, 0, FAKE, None, FAKE,
