@@ -5,18 +5,17 @@
 // block scale is applied inside the matrix unit.  On CDNA4,
 // v_mfma_scale_f32_32x32x64_f8f6f4 takes one E8M0 scale per lane per 32-element
 // K block, which is exactly the MX block, so codes go from LDS straight into
-// the MFMA (operand layouts in k_gemm_mx below).  The NVFP4 GEMM lives in
+// the MFMA (operand layouts at MxFrag below).  The NVFP4 GEMM lives in
 // bsq_gemm_nvfp4.hip.
 //
 // Tiling: 256 x 256 output tile per 512-thread workgroup (8 waves as 2 x 4,
 // each 128 (M) x 64 (N) = 4 x 2 MFMA tiles of 32 x 32); each wave computes
 // D = B_tile . A_tile^T so that every lane holds consecutive output columns.
-//  * k_gemm_mx (K % 512 == 0, aligned operands): 64 code bytes per row per
+//  * k_gemm_mx_pp (K % 512 == 0, aligned operands): 64 code bytes per row per
 //    stage (K 64 for MXFP8, 128 for MXFP4) staged in LDS by global -> LDS
-//    direct loads four stages ahead (four stage buffers), scales 16 bytes per
-//    row per period of 8 / 4 stages, one barrier per stage; each wave reads the
-//    next stage's fragments into a second register set while the MFMAs of the
-//    current stage run.
+//    direct loads four stages ahead, scales 16 bytes per row per period of
+//    8 / 4 stages; the two waves of each SIMD alternate between the MFMAs of
+//    one stage and the fragment reads of the next (layout and schedule below).
 //  * k_gemm (any K): the general path, register-staged, one stage ahead.
 //
 // K order inside a stage: an MFMA only needs A and B to agree on which K index
@@ -297,13 +296,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
 // bytes, then B codes; 16-byte chunk c of row r in slot c ^ ((r >> 2) & 3),
 // which keeps the fragment reads of 16 consecutive rows on distinct banks),
 // then two scale buffers of 8 KiB (16 scale bytes of each of the 256 A rows
-// and 256 B rows: four MXFP4 stages or eight MXFP8 stages).  Wave w stages rows
-// 32 w .. 32 w + 31 of both operands' codes every stage (4 direct loads of 16
-// rows x 64 bytes) and 64 rows of one operand's scales once per scale period
-// (one direct load of 64 rows x 16 bytes).  The kernel is bound by the number
-// of L2 requests, not bytes: a row's scales are fetched as one 16-byte piece
-// per period instead of one dword per stage, which removes over a third of the
-// requests.
+// and 256 B rows: four MXFP4 stages or eight MXFP8 stages).  A row's scales
+// are fetched as one 16-byte piece per period instead of one dword per stage,
+// which removes over a third of the L2 requests.
 constexpr int kMxRowB = 64;
 constexpr int kMxCodeB = 256 * kMxRowB;
 constexpr int kMxStageB = 2 * kMxCodeB;                  // 32 KiB of codes per stage
@@ -311,34 +306,12 @@ constexpr int kMxStages = 4;
 constexpr int kMxScOff = kMxStages * kMxStageB;          // scale buffers after the code buffers
 constexpr int kMxScB = 2 * 256 * 16;                     // one scale period, both operands
 constexpr int kMxLds = kMxScOff + 2 * kMxScB > kEpiLds ? kMxScOff + 2 * kMxScB : kEpiLds;
-constexpr int kMxDma = 4;                                // code loads per wave per stage
 static_assert(kMxLds <= 160 * 1024, "MX staged LDS plan");
 
 // Stages per scale period: 16 bytes of a row hold 4 MXFP4 stages (128 K
 // each, 4 blocks) or 8 MXFP8 stages (64 K each, 2 blocks).
 template <int FMT>
 constexpr int mx_period() { return FMT == kMXFP8 ? 8 : 4; }
-
-struct MxLoadMap {
-  uint32_t code[4];                                      // byte offset of this lane's 16 bytes
-  uint32_t scale;                                        // byte offset of this lane's scale row
-};
-
-template <int FMT>
-__device__ __forceinline__ void mx_stage(const uint8_t* ac, const uint8_t* bc, const MxLoadMap& lm,
-                                         int64_t kt, uint32_t st, int w) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint8_t* base = (i < 2 ? ac : bc) + kt * kMxRowB;
-    dma_to_lds<16>(base, lm.code[i], st + (i >> 1) * kMxCodeB + (w * 32 + (i & 1) * 16) * kMxRowB);
-  }
-}
-
-// Scale period q (16 bytes per row) into scale buffer `sb`.
-__device__ __forceinline__ void mx_stage_scales(const uint8_t* as, const uint8_t* bs,
-                                                const MxLoadMap& lm, int64_t q, uint32_t sb, int w) {
-  dma_to_lds<16>((w < 4 ? as : bs) + q * 16, lm.scale, sb + (w >> 2) * (256 * 16) + (w & 3) * (64 * 16));
-}
 
 // Fragments and scale operands of one stage for one wave.  MXFP8: fa[0]/fa[1]
 // are bytes 0-15 / 16-31 of the operand (chunks h and 2 + h); MXFP4: fa[s] is
@@ -399,104 +372,110 @@ __device__ __forceinline__ void mx_mfma(floatx16 (&acc)[4][2], const MxFrag& F) 
                                                                 (int)F.sb[ni], s, (int)F.sa[mi]);
 }
 
-// Reads issued after MFMA I: [lo(I), lo(I + 1)), spread over the first 8 MFMAs
-// (MXFP8) or the first 12 (MXFP4) so that they complete before the barrier.
-template <int FMT>
-__host__ __device__ constexpr int mx_rd_lo(int i) {
-  return FMT == kMXFP8 ? (i * 18 + 7) / 8 > 18 ? 18 : (i * 18 + 7) / 8
-                       : (i * 18 + 11) / 12 > 18 ? 18 : (i * 18 + 11) / 12;
-}
+// ---------------------------------------------------------------- ping-pong kernel
+//
+// The matrix pipe of every SIMD is fed by one wave while its sibling wave
+// reads fragments.  The two waves of a SIMD belong to different
+// groups (waves 0-3 compute rows 0-127 of the tile, waves 4-7 rows 128-255);
+// time is cut into slots separated by workgroup barriers.  Group 0 runs the
+// MFMAs of stage j on slot 2j and reads all fragments of stage j + 1 on slot
+// 2j + 1; group 1 reads stage j on slot 2j and runs its MFMAs on slot 2j + 1.
+// Staging: on slot 2j + 1 both groups issue stage j + 4 into the buffer of
+// stage j (read by group 0 on slot 2j - 1 and by group 1 on slot 2j), group 0
+// the A rows and group 1 the B rows (wave w: rows 64 w .. 64 w + 63, four
+// direct loads of 16 rows x 64 bytes), each with one scale load (the rows'
+// 16 bytes of a scale period at the period's first stage, else lane 0
+// reloading its own 16 bytes in place) so that every issue is five loads.
+// Stage j is issued on slot 2j - 7 and waited for by its issuing waves on slot
+// 2j - 2 (their loads of stages j + 1 and j + 2 may stay in flight), before the
+// barrier that precedes its first read on slot 2j - 1.  A scale period q is
+// issued with code stage q P on slot 2 q P - 7 into the buffer of period q - 2,
+// whose last read was on slot 2 q P - 2 P - 2 (P >= 4 stages per period).
+constexpr int kMxPpLoads = 5;                            // loads per issued stage per wave
 
-template <int FMT, int I>
-__device__ __forceinline__ void mx_step(floatx16 (&acc)[4][2], const MxFrag& C, MxFrag& N,
-                                        const uint8_t* nbuf, const uint8_t* nsbuf, int nsb0, int wm,
-                                        int wn, int h, int l32) {
-  mx_mfma<FMT, I>(acc, C);
-  constexpr int lo = mx_rd_lo<FMT>(I), hi = mx_rd_lo<FMT>(I + 1);
-  if (lo + 0 < hi) mx_read<FMT, lo + 0 < 18 ? lo + 0 : 17>(N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  if (lo + 1 < hi) mx_read<FMT, lo + 1 < 18 ? lo + 1 : 17>(N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  if (lo + 2 < hi) mx_read<FMT, lo + 2 < 18 ? lo + 2 : 17>(N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Everything a stage needs besides the fragments (wave-uniform).
-struct MxCtx {
-  const uint8_t* ac;
-  const uint8_t* as;
-  const uint8_t* bc;
-  const uint8_t* bs;
-  uint8_t* smem;
-  uint32_t smem_lds;
-  int64_t KT, NP;            // stages, scale periods
-  int w;
+struct MxPpSrc {
+  const uint8_t* codes;                                  // this group's operand
+  const uint8_t* scales;
+  uint32_t code_off[4];                                  // this lane's byte offsets (stage 0)
+  uint32_t scale_off;
+  uint32_t code_lds, scale_lds;                          // this wave's LDS rows (stage buffer 0, period buffer 0)
+  int64_t KT, NP;
 };
 
-// Scale slot of stage kt (one direct load every stage, so that this wave's
-// load count per stage is fixed): at a period start (kt % period == 0) the
-// scales of period q + 1 into its buffer; otherwise lane 0 reloads its own 16
-// bytes of the current period into the place they already occupy (one L2
-// request, same bytes).
-__device__ __forceinline__ void mx_scale_slot(const MxCtx& x, const MxLoadMap& lm, int64_t q,
-                                              int64_t ph, int lane) {
-  if (ph == 0) {
-    const int64_t nq = q + 1 < x.NP ? q + 1 : x.NP - 1;
-    mx_stage_scales(x.as, x.bs, lm, nq, x.smem_lds + kMxScOff + (uint32_t)((q + 1) & 1) * kMxScB, x.w);
-  } else if (lane == 0) {
-    mx_stage_scales(x.as, x.bs, lm, q, x.smem_lds + kMxScOff + (uint32_t)(q & 1) * kMxScB, x.w);
-  }
-}
-
-// Stage kt (P = kt & 1): wait until stage kt + 1 has landed (this wave's loads,
-// then everyone's), the scale slot, stage kt + 4 into the buffer of stage kt
-// (whose fragments are in registers), then the MFMAs of kt on C with the
-// fragment reads of kt + 1 into N interleaved.  This wave's loads issued after
-// stage kt + 1's are the scale slots and stages of kt + 2 and kt + 3, so at
-// most 2 (1 + kMxDma) may remain.  A period's scales are issued before the
-// code stage four ahead, which is waited for before that period's first read.
-template <int FMT, int P>
-__device__ __forceinline__ void mx_iter(floatx16 (&acc)[4][2], MxFrag& C, MxFrag& N,
-                                        const MxCtx& x, const MxLoadMap& lm, int64_t kt, int wm,
-                                        int wn, int h, int l32, int lane) {
+// Issue stage s (clamped to the last) and its scale slot.
+template <int FMT>
+__device__ __forceinline__ void mx_pp_issue(const MxPpSrc& x, int64_t s, int lane) {
   constexpr int PER = mx_period<FMT>();
-  wait_vmcnt<2 * (1 + kMxDma)>();
-  lds_barrier();                               // everyone's; all fragments of kt are in registers
-  const int64_t q = kt / PER, ph = kt - q * PER;
-  mx_scale_slot(x, lm, q, ph, lane);
-  const int64_t nk = kt + 4 < x.KT ? kt + 4 : x.KT - 1;
-  mx_stage<FMT>(x.ac, x.bc, lm, nk, x.smem_lds + (uint32_t)(kt & 3) * kMxStageB, x.w);
-  const uint8_t* nbuf = x.smem + ((kt + 1) & 3) * kMxStageB;
-  const int64_t nq = (kt + 1) / PER;
-  const uint8_t* nsbuf = x.smem + kMxScOff + (nq & 1) * kMxScB;
-  const int nsb0 = (int)(kt + 1 - nq * PER) * (FMT == kMXFP8 ? 2 : 4);
-  mx_step<FMT, 0>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  mx_step<FMT, 1>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  mx_step<FMT, 2>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  mx_step<FMT, 3>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  mx_step<FMT, 4>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  mx_step<FMT, 5>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  mx_step<FMT, 6>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  mx_step<FMT, 7>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  if (FMT == kMXFP4) {
-    mx_step<FMT, 8>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-    mx_step<FMT, 9>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-    mx_step<FMT, 10>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-    mx_step<FMT, 11>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-    mx_step<FMT, 12>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-    mx_step<FMT, 13>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-    mx_step<FMT, 14>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-    mx_step<FMT, 15>(acc, C, N, nbuf, nsbuf, nsb0, wm, wn, h, l32);
-  }
+  const int64_t cs = s < x.KT ? s : x.KT - 1;
+  const uint32_t buf = x.code_lds + (uint32_t)(s & 3) * kMxStageB;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma_to_lds<16>(x.codes + cs * kMxRowB, x.code_off[i], buf + i * 16 * kMxRowB);
+  const int64_t q = s / PER, cq = q < x.NP ? q : x.NP - 1;
+  if (s - q * PER == 0)
+    dma_to_lds<16>(x.scales + cq * 16, x.scale_off, x.scale_lds + (uint32_t)(q & 1) * kMxScB);
+  else if (lane == 0)
+    dma_to_lds<16>(x.scales + cq * 16, x.scale_off, x.scale_lds + (uint32_t)(q & 1) * kMxScB);
 }
 
-template <int FMT, int Q>
-__device__ __forceinline__ void mx_read_all(MxFrag& F, const uint8_t* buf, const uint8_t* sbuf,
-                                            int wm, int wn, int h, int l32) {
-  mx_read<FMT, Q>(F, buf, sbuf, 0, wm, wn, h, l32);
-  if constexpr (Q + 1 < 18) mx_read_all<FMT, Q + 1>(F, buf, sbuf, wm, wn, h, l32);
+// Slot boundaries for register-only work.  The barriers order memory accesses
+// only, and the MFMAs touch no memory, so without these empty statements the
+// compiler may move a slot's MFMAs across a barrier into the other slot.  An
+// asm statement that reads and writes the accumulators (or the fragments)
+// keeps the MFMAs that produce (or consume) them on its side.
+__device__ __forceinline__ void pin_acc(floatx16 (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]));
+}
+__device__ __forceinline__ void pin_frag(MxFrag& F) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(F.fa[0][i]), "+v"(F.fa[1][i]), "+v"(F.sa[i]));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(F.fb[0][i]), "+v"(F.fb[1][i]), "+v"(F.sb[i]));
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void k_gemm_mx(
+__device__ __forceinline__ void mx_pp_mfmas(floatx16 (&acc)[4][2], const MxFrag& F) {
+  mx_mfma<FMT, 0>(acc, F);
+  mx_mfma<FMT, 1>(acc, F);
+  mx_mfma<FMT, 2>(acc, F);
+  mx_mfma<FMT, 3>(acc, F);
+  mx_mfma<FMT, 4>(acc, F);
+  mx_mfma<FMT, 5>(acc, F);
+  mx_mfma<FMT, 6>(acc, F);
+  mx_mfma<FMT, 7>(acc, F);
+  if (FMT == kMXFP4) {
+    mx_mfma<FMT, 8>(acc, F);
+    mx_mfma<FMT, 9>(acc, F);
+    mx_mfma<FMT, 10>(acc, F);
+    mx_mfma<FMT, 11>(acc, F);
+    mx_mfma<FMT, 12>(acc, F);
+    mx_mfma<FMT, 13>(acc, F);
+    mx_mfma<FMT, 14>(acc, F);
+    mx_mfma<FMT, 15>(acc, F);
+  }
+}
+
+// All fragments and scale operands of stage s.
+template <int FMT, int Q>
+__device__ __forceinline__ void mx_pp_read_from(MxFrag& F, const uint8_t* buf, const uint8_t* sbuf,
+                                                int sb0, int wm, int wn, int h, int l32) {
+  mx_read<FMT, Q>(F, buf, sbuf, sb0, wm, wn, h, l32);
+  if constexpr (Q + 1 < 18) mx_pp_read_from<FMT, Q + 1>(F, buf, sbuf, sb0, wm, wn, h, l32);
+}
+template <int FMT>
+__device__ __forceinline__ void mx_pp_read(MxFrag& F, const uint8_t* smem, int64_t s, int wm, int wn,
+                                           int h, int l32) {
+  constexpr int PER = mx_period<FMT>();
+  const int64_t q = s / PER;
+  const int sb0 = (int)(s - q * PER) * (FMT == kMXFP8 ? 2 : 4);
+  mx_pp_read_from<FMT, 0>(F, smem + (s & 3) * kMxStageB, smem + kMxScOff + (q & 1) * kMxScB, sb0,
+                          wm, wn, h, l32);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_gemm_mx_pp(
     int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
     const uint8_t* b_codes, const uint8_t* b_scales, uint16_t* __restrict__ c, int64_t ldc,
     int tiles_m, int tiles_n, int vec_store) {
@@ -507,33 +486,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(wave);
+  // group and wave within the group, scalar: they address the direct loads
+  const int gs = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int w = __builtin_amdgcn_readfirstlane(wave & 3);
   const int64_t code_ld = FMT == kMXFP8 ? K : K / 2, scale_ld = K / 32;
-  constexpr int P = mx_period<FMT>();
-  MxCtx x;
-  x.ac = a_codes;
-  x.as = a_scales;
-  x.bc = b_codes;
-  x.bs = b_scales;
-  x.smem = smem;
-  x.smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  x.KT = code_ld / kMxRowB;                              // stages (a multiple of the period)
-  x.NP = x.KT / P;
-  x.w = w;
-  MxLoadMap lm;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = w * 32 + (i & 1) * 16 + (lane >> 2);  // row within the tile
-    const int64_t base = i < 2 ? m0 : n0, rows = i < 2 ? M : N;
-    const int64_t gr = base + rr < rows ? base + rr : rows - 1;
-    lm.code[i] = (uint32_t)(gr * code_ld + (((lane & 3) ^ ((rr >> 2) & 3)) << 4));
-  }
+  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  MxPpSrc x;
+  x.codes = gs == 0 ? a_codes : b_codes;
+  x.scales = gs == 0 ? a_scales : b_scales;
+  x.KT = code_ld / kMxRowB;                              // a multiple of 4 (K % 512 == 0)
+  x.NP = x.KT / mx_period<FMT>();
   {
-    const int rr = (w & 3) * 64 + lane;
-    const int64_t base = w < 4 ? m0 : n0, rows = w < 4 ? M : N;
+    const int64_t base = gs == 0 ? m0 : n0, rows = gs == 0 ? M : N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = w * 64 + i * 16 + (lane >> 2);      // row within the tile
+      const int64_t gr = base + rr < rows ? base + rr : rows - 1;
+      x.code_off[i] = (uint32_t)(gr * code_ld + (((lane & 3) ^ ((rr >> 2) & 3)) << 4));
+    }
+    const int rr = w * 64 + lane;
     const int64_t gr = base + rr < rows ? base + rr : rows - 1;
-    lm.scale = (uint32_t)(gr * scale_ld);
+    x.scale_off = (uint32_t)(gr * scale_ld);
   }
+  x.code_lds = smem_lds + (uint32_t)gs * kMxCodeB + (uint32_t)(w * 64) * kMxRowB;
+  x.scale_lds = smem_lds + kMxScOff + (uint32_t)gs * (256 * 16) + (uint32_t)(w * 64) * 16;
+
   floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -542,23 +519,38 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // prologue: the scales of period 0 and the code stages 0..3, each stage
-  // preceded by a scale slot's worth of loads so the per-stage count is fixed
-  mx_stage_scales(a_scales, b_scales, lm, 0, x.smem_lds + kMxScOff, w);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (k > 0 && lane == 0) mx_stage_scales(a_scales, b_scales, lm, 0, x.smem_lds + kMxScOff, w);
-    mx_stage<FMT>(a_codes, b_codes, lm, k < x.KT ? k : x.KT - 1, x.smem_lds + k * kMxStageB, w);
-  }
-  wait_vmcnt<3 * (1 + kMxDma)>();              // period-0 scales and stage 0 in
+  mx_pp_issue<FMT>(x, 0, lane);
+  mx_pp_issue<FMT>(x, 1, lane);
+  mx_pp_issue<FMT>(x, 2, lane);
+  mx_pp_issue<FMT>(x, 3, lane);
+  wait_vmcnt<3 * kMxPpLoads>();                          // stage 0 and period 0 in
   lds_barrier();
-  MxFrag F0, F1;
-  mx_read_all<FMT, 0>(F0, smem, smem + kMxScOff, wm, wn, h, l32);
-  for (int64_t kt = 0; kt < x.KT; kt += 2) {   // KT is even (a multiple of the period)
-    mx_iter<FMT, 0>(acc, F0, F1, x, lm, kt, wm, wn, h, l32, lane);
-    mx_iter<FMT, 1>(acc, F1, F0, x, lm, kt + 1, wm, wn, h, l32, lane);
+  MxFrag F;
+  if (gs == 0) {
+    mx_pp_read<FMT>(F, smem, 0, wm, wn, h, l32);
+    for (int64_t j = 0; j < x.KT; ++j) {
+      pin_frag(F);
+      mx_pp_mfmas<FMT>(acc, F);                          // slot 2j
+      pin_acc(acc);
+      wait_vmcnt<2 * kMxPpLoads>();                      // stage j + 1 in
+      lds_barrier();
+      mx_pp_read<FMT>(F, smem, j + 1, wm, wn, h, l32);   // slot 2j + 1
+      mx_pp_issue<FMT>(x, j + 4, lane);
+      lds_barrier();
+    }
+  } else {
+    for (int64_t j = 0; j < x.KT; ++j) {
+      mx_pp_read<FMT>(F, smem, j, wm, wn, h, l32);       // slot 2j
+      wait_vmcnt<2 * kMxPpLoads>();                      // stage j + 1 in
+      lds_barrier();
+      pin_frag(F);
+      mx_pp_issue<FMT>(x, j + 4, lane);                  // slot 2j + 1
+      mx_pp_mfmas<FMT>(acc, F);
+      pin_acc(acc);
+      lds_barrier();
+    }
   }
-  wait_vmcnt<0>();                             // the clamped tail loads land in LDS the epilogue reuses
+  wait_vmcnt<0>();                                       // the clamped tail loads land in LDS the epilogue reuses
   lds_barrier();
   store_tile_bf16(acc, smem, 1.0f, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
 }
@@ -596,12 +588,12 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   static bool mx_attr_set = false;
   if (staged) {
     if (!mx_attr_set) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx<FMT>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx_pp<FMT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds) != hipSuccess)
         return hipErrorInvalidConfiguration;
       mx_attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemm_mx<FMT>), grid, block, kMxLds, s, M, N, K, ac, as, bc, bs, cp, ldc,
+    hipLaunchKernelGGL((k_gemm_mx_pp<FMT>), grid, block, kMxLds, s, M, N, K, ac, as, bc, bs, cp, ldc,
                        tiles_m, tiles_n, vec_store ? 1 : 0);
     return hipGetLastError();
   }
