@@ -67,7 +67,10 @@ def test_nvfp4_shape_sweep(M, N, K):
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("M,N,K", [(16, 16, 32), (48, 272, 96), (256, 256, 256), (512, 768, 384),
-                                   (300, 48, 4096)])
+                                   (300, 48, 4096),
+                                   # staged kernel (K % 512 == 0): fewest stages (one scale
+                                   # period), ragged tiles, and an odd number of periods
+                                   (256, 256, 512), (520, 300, 512), (768, 1024, 1536)])
 def test_mx_shape_sweep(fmt, M, N, K):
     announce("mx sweep", fmt, M, N, K)
     A = synth.bf16_tensor((M, K), 3000 + M + K, device="cuda")
