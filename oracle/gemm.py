@@ -11,6 +11,8 @@ operands are K-major (quantized along K).
 * NVFP4: deq = e2m1(code) * e4m3(S_block); alpha = s_dec(A) * s_dec(B) with
   s_dec the float32 per-tensor decode scale of each operand.
 * MX:    deq = element(code) * 2**(E - 127); alpha = 1.
+* FP8 per-tensor (the post's FP8 baseline, oracle/quantize.py): deq =
+  e4m3(code); alpha = s_dec(A) * s_dec(B) with the float32 FP8 decode scales.
 
 Tolerance (a reading): the GPU result is BF16, whose own rounding is up to
 half a BF16 ulp, which at these output sizes already exceeds 1e-2 * rms by
@@ -21,7 +23,7 @@ itself.  So the test passes when
 import numpy as np
 
 from . import formats as F
-from .quantize import nvfp4_scale_dec
+from .quantize import fp8_scale_dec, nvfp4_scale_dec
 
 
 def dequant_nvfp4(codes, scales):
@@ -83,3 +85,14 @@ def tolerance_report(c_gpu, c_ref):
         frac_equal_rne=float(np.mean(c_gpu == F.f64_to_bf16_rne(c_ref))) if c_ref.size else 1.0,
         passed=bool(excess <= 1e-2 * rms) if c_ref.size else True,
     )
+
+
+def fp8_alpha(a_amax, b_amax):
+    """alpha = s_dec(A) * s_dec(B) of two per-tensor FP8 operands, in float64."""
+    return np.float64(fp8_scale_dec(a_amax)) * np.float64(fp8_scale_dec(b_amax))
+
+
+def gemm_fp8(a_codes, a_amax, b_codes, b_amax):
+    A = F.e4m3_decode(a_codes).astype(np.float64)
+    B = F.e4m3_decode(b_codes).astype(np.float64)
+    return fp8_alpha(a_amax, b_amax) * (A @ B.T)

@@ -217,3 +217,52 @@ def quantize_transpose(x, fmt="nvfp4", block_rows=1, rnd="rne", seed=0, offset=0
         ra = ca = None
     return dict(row_codes=rc, row_scales=rs, row_amax=ra,
                 col_codes=cc, col_scales=cs, col_amax=ca)
+
+
+# --------------------------------------------------------------------------
+# Per-tensor FP8: the FP8 baseline the NVFP4 post measures against
+# --------------------------------------------------------------------------
+#
+# NVFP4 pretraining post: the paragraph after the example script names the
+# FP8 baseline run (MaxText quantization=te_fp8_delayedscaling), and section
+# "Performance results" (Table 1, Figure 2) compares NVFP4 with it.  The pages
+# give no formula.  Readings: every tensor is E4M3 (OCP E4M3FN) under one
+# float32 per-tensor scale taken from the tensor's own amax (the amax history
+# of delayed scaling, which spans training steps, is left out):
+#     s_enc = 448 / amax (1 if amax == 0, at most FLT_MAX), s_dec = 1 / s_enc,
+#     code  = E4M3_RNE_sat(x * s_enc)      (one float32 multiply),
+# and the column output is the same rule applied to x^T (same amax).
+
+FP8_MAX = 448.0
+
+
+def fp8_scale_enc(amax):
+    """Per-tensor FP8 encode scale 448 / amax (float32), 1 for amax == 0."""
+    amax = np.float32(amax)
+    if amax == 0:
+        return np.float32(1.0)
+    with np.errstate(over="ignore", divide="ignore"):
+        s = np.float32(FP8_MAX) / amax
+    return np.float32(min(s, F.FLT_MAX))
+
+
+def fp8_scale_dec(amax):
+    """Per-tensor FP8 decode scale 1 / s_enc (float32)."""
+    return np.float32(np.float32(1.0) / fp8_scale_enc(amax))
+
+
+def fp8_quantize(x, amax=None):
+    """Per-tensor FP8 of x [R, C]: (codes uint8 [R, C] E4M3, amax float32)."""
+    y = as_f32(x)
+    if amax is None:
+        amax = tensor_amax(y)
+    v = (y * fp8_scale_enc(amax)).astype(np.float32)
+    return F.e4m3_encode_rne(v), np.float32(amax)
+
+
+def fp8_quantize_transpose(x):
+    """Row (x) and column (x^T) per-tensor FP8 outputs under one amax."""
+    y = as_f32(x)
+    rc, amax = fp8_quantize(y)
+    cc, _ = fp8_quantize(np.ascontiguousarray(y.T), amax)
+    return dict(row_codes=rc, col_codes=cc, amax=amax)
