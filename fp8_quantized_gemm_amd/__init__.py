@@ -1,4 +1,5 @@
-"""Block-scaled (NVFP4 / MXFP4 / MXFP8) quantize + GEMM on MI355X.
+"""Block-scaled (NVFP4 / MXFP4 / MXFP8) quantize + GEMM on MI355X, with the
+per-tensor FP8 baseline (format "fp8") for comparison.
 
 Thin Python binding over the C ABI of libbsq.so (include/bsq.h): argument
 marshalling only.  PyTorch supplies device memory and the current stream;
@@ -16,10 +17,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbsq.so")
 
 BSQ_OK, BSQ_EINVAL, BSQ_EUNSUPPORTED, BSQ_EHIP = 0, 1, 2, 3
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "mxfp8": 2}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "mxfp8": 2, "fp8": 3}
 ROUNDING = {"rne": 0, "sr": 1}
-ABI_SYMBOLS = ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "bs_gemm",
-               "bsq_status_string")
+ABI_SYMBOLS = ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "fp8_quantize_transpose",
+               "bs_gemm", "bsq_status_string")
 
 
 class BsqError(RuntimeError):
@@ -45,8 +46,10 @@ def lib():
         L.mx_quantize.argtypes = [P, I64, I64, I, I, U64, U32, P, P, P]
         L.quantize_transpose.argtypes = [P, I64, I64, I, I, I, U64, U32, I, U16,
                                          P, P, P, P, P, P, P]
+        L.fp8_quantize_transpose.argtypes = [P, I64, I64, P, P, P, P]
         L.bs_gemm.argtypes = [I, I64, I64, I64, P, P, P, P, P, P, P, I64, P]
-        for fn in ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "bs_gemm"):
+        for fn in ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "fp8_quantize_transpose",
+                   "bs_gemm"):
             getattr(L, fn).restype = I
         L.bsq_status_string.argtypes = [I]
         L.bsq_status_string.restype = ctypes.c_char_p
@@ -139,11 +142,27 @@ def quantize_transpose(x, fmt="nvfp4", block_rows=1, rnd="rne", seed=0, offset=0
     return out
 
 
+def fp8_quantize_transpose(x, row=True, col=True):
+    """Per-tensor FP8 (E4M3, s_enc = 448 / amax) of x [R, C] and of x^T.
+
+    Returns a dict with row_codes [R, C], col_codes [C, R] (None when skipped)
+    and amax (f32 [1])."""
+    x = _check_input(x)
+    R, C = x.shape
+    rc = _u8((R, C), x.device) if row else None
+    cc = _u8((C, R), x.device) if col else None
+    amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    st = lib().fp8_quantize_transpose(_ptr(x), R, C, _ptr(rc), _ptr(cc), _ptr(amax), _stream(x.device))
+    _check("fp8_quantize_transpose", st)
+    return dict(row_codes=rc, col_codes=cc, amax=amax)
+
+
 def bs_gemm(fmt, a_codes, a_scales, b_codes, b_scales, a_amax=None, b_amax=None, K=None, out=None):
-    """C [M, N] bf16 = alpha * deq(A) . deq(B)^T with A, B K-major block-scaled operands."""
+    """C [M, N] bf16 = alpha * deq(A) . deq(B)^T with A, B K-major block-scaled operands
+    (per-tensor "fp8": scales None, amaxes required)."""
     M, N = a_codes.shape[0], b_codes.shape[0]
     if K is None:
-        K = a_codes.shape[1] * (1 if fmt == "mxfp8" else 2)
+        K = a_codes.shape[1] * (1 if fmt in ("mxfp8", "fp8") else 2)
     dev = a_codes.device
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)

@@ -75,7 +75,8 @@ bsq_status mx_quantize(const void* x, int64_t rows, int64_t cols, bsq_format fmt
                        bsq_rounding rnd, uint64_t seed, uint32_t offset, uint8_t* codes,
                        uint8_t* scales, void* stream) {
   if (rows < 0 || cols < 0 || cols % 32 != 0) return BSQ_EINVAL;
-  if (fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8) return fmt == BSQ_NVFP4 ? BSQ_EUNSUPPORTED : BSQ_EINVAL;
+  if (fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8)
+    return fmt == BSQ_NVFP4 || fmt == BSQ_FP8 ? BSQ_EUNSUPPORTED : BSQ_EINVAL;
   if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
   if (fmt == BSQ_MXFP8 && rnd == BSQ_SR) return BSQ_EUNSUPPORTED;
   const int64_t n = rows * cols;
@@ -93,6 +94,7 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
                               int rht_col, uint16_t rht_signs, uint8_t* codes_row,
                               uint8_t* scales_row, float* amax_row, uint8_t* codes_col,
                               uint8_t* scales_col, float* amax_col, void* stream) {
+  if (fmt == BSQ_FP8) return BSQ_EUNSUPPORTED;      // fp8_quantize_transpose
   if (fmt != BSQ_NVFP4 && fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8) return BSQ_EINVAL;
   const bool nv = fmt == BSQ_NVFP4;
   const int blk = nv ? 16 : 32;
@@ -140,11 +142,28 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
   return hip_status(e);
 }
 
+bsq_status fp8_quantize_transpose(const void* x, int64_t rows, int64_t cols, uint8_t* codes_row,
+                                  uint8_t* codes_col, float* amax, void* stream) {
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return BSQ_EINVAL;
+  if (!amax || !aligned4(amax)) return BSQ_EINVAL;
+  if (!codes_row && !codes_col) return BSQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (rows * cols == 0) return hip_status(bsq::launch_zero_amax(amax, nullptr, s));
+  if (!x || !aligned16(x) || !aligned16_or_null(codes_row) || !aligned16_or_null(codes_col))
+    return BSQ_EINVAL;
+  hipError_t e = bsq::launch_zero_amax(amax, nullptr, s);
+  if (e != hipSuccess) return BSQ_EHIP;
+  e = bsq::launch_amax_flat(x, rows * cols / 8, false, 0, amax, nullptr, s);
+  if (e != hipSuccess) return BSQ_EHIP;
+  return hip_status(bsq::launch_fp8_qt(x, rows, cols, amax, codes_row, codes_col, s));
+}
+
 bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                    const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
                    const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,
                    void* stream) {
-  if (fmt != BSQ_NVFP4 && fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8) return BSQ_EINVAL;
+  if (fmt != BSQ_NVFP4 && fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8 && fmt != BSQ_FP8) return BSQ_EINVAL;
+  const bool per_tensor = fmt == BSQ_NVFP4 || fmt == BSQ_FP8;   // alpha from the two amaxes
   if (M < 0 || N < 0 || K < 0) return BSQ_EINVAL;
   if (K % (fmt == BSQ_NVFP4 ? 16 : 32) != 0) return BSQ_EINVAL;
   if (ldc < N || ldc < 0) return BSQ_EINVAL;
@@ -152,12 +171,13 @@ bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_
   if (M == 0 || N == 0) return BSQ_OK;
   if (!c || ((reinterpret_cast<uintptr_t>(c) & 1u) != 0)) return BSQ_EINVAL;
   if (K > 0) {
-    if (!a_codes || !a_scales || !b_codes || !b_scales) return BSQ_EINVAL;
-    if (fmt == BSQ_NVFP4 && (!a_amax || !b_amax)) return BSQ_EINVAL;
-  } else if (fmt == BSQ_NVFP4 && (!a_amax || !b_amax)) {
-    return BSQ_EINVAL;
+    if (!a_codes || !b_codes) return BSQ_EINVAL;
+    if (fmt != BSQ_FP8 && (!a_scales || !b_scales)) return BSQ_EINVAL;
   }
-  const bsq::Fmt f = fmt == BSQ_NVFP4 ? bsq::kNVFP4 : (fmt == BSQ_MXFP4 ? bsq::kMXFP4 : bsq::kMXFP8);
+  if (per_tensor && (!a_amax || !b_amax)) return BSQ_EINVAL;
+  const bsq::Fmt f = fmt == BSQ_NVFP4 ? bsq::kNVFP4
+                     : fmt == BSQ_MXFP4 ? bsq::kMXFP4
+                     : fmt == BSQ_MXFP8 ? bsq::kMXFP8 : bsq::kFP8;
   return hip_status(bsq::launch_gemm(f, M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales,
                                      b_amax, c, ldc, static_cast<hipStream_t>(stream)));
 }

@@ -1,5 +1,7 @@
 // MX block-scaled GEMM for gfx950: C[M, N] (BF16) = A[M, K] . B[N, K]^T with
-// MXFP8 (E4M3) or MXFP4 (E2M1) codes and one E8M0 scale per 32 K-elements.
+// MXFP8 (E4M3) or MXFP4 (E2M1) codes and one E8M0 scale per 32 K-elements;
+// the same kernels run the per-tensor FP8 baseline (E4M3 codes, unit block
+// scales, alpha = s_dec(A) * s_dec(B) from the two amaxes).
 //
 // HN page opcode84 (MXFP8 / MXFP4 GEMMs on the OCP Microscaling formats): the
 // block scale is applied inside the matrix unit.  On CDNA4,
@@ -32,7 +34,7 @@ constexpr int kBM = 256, kBN = 256, kThreads = 512;
 template <int FMT>
 struct Cfg {
   static constexpr int BK = FMT == kMXFP4 ? 256 : 128;                 // K elements per stage
-  static constexpr int RB = FMT == kMXFP8 ? BK : BK / 2;               // code bytes per row per stage
+  static constexpr int RB = fp8_elems(FMT) ? BK : BK / 2;              // code bytes per row per stage
   static constexpr int SB = FMT == kNVFP4 ? BK / 16 : BK / 32;         // scale bytes per row per stage
   static constexpr int LDR = RB + 16;                                  // padded LDS row stride
   static constexpr int CODE_BYTES = kBM * LDR;                         // per operand per stage
@@ -93,9 +95,10 @@ __device__ __forceinline__ void load_stage(Stage<FMT>& st, const uint8_t* __rest
       st.code[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
-  // scales: thread t < 256 loads row t's SB bytes (SB is 4 or 8)
-  st.scale[0] = st.scale[1] = 0;
-  if (t < kBM) {
+  // scales: thread t < 256 loads row t's SB bytes (SB is 4 or 8); per-tensor
+  // FP8 has none and uses the E8M0 unit scale (127) for every block
+  st.scale[0] = st.scale[1] = FMT == kFP8 ? 0x7F7F7F7Fu : 0u;
+  if (FMT != kFP8 && t < kBM) {
     int64_t gr = row0 + t;
     gr = gr < rows ? gr : rows - 1;
     const int64_t sb = kt * C::SB;
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   const int wm = wave >> 2, wn = wave & 3;            // 2 x 4 waves
   const int h = lane >> 5, l32 = lane & 31;
 
-  const int64_t code_ld = FMT == kMXFP8 ? K : K / 2;
+  const int64_t code_ld = fp8_elems(FMT) ? K : K / 2;
   const int64_t scale_ld = FMT == kNVFP4 ? K / 16 : K / 32;
   const int64_t KT = (K + C::BK - 1) / C::BK;
 
@@ -211,24 +214,24 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
       //    instruction and bytes 16-31 to the second, each block split over the
       //    two lane halves; here step s uses blocks 2s and 2s+1, lane half h
       //    taking elements [16h, 16h+16) of each.
-      constexpr int FMTC = FMT == kMXFP8 ? 0 : 4;     // cbsz / blgp operand type
+      constexpr int FMTC = fp8_elems(FMT) ? 0 : 4;    // cbsz / blgp operand type
       uint32_t sca[4], scb[2];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         const int row = wm * 128 + mi * 32 + l32;
-        sca[mi] = FMT == kMXFP8 ? (*reinterpret_cast<const uint32_t*>(LSa + row * 4) >> (8 * h))
+        sca[mi] = fp8_elems(FMT) ? (*reinterpret_cast<const uint32_t*>(LSa + row * 4) >> (8 * h))
                                 : *reinterpret_cast<const uint32_t*>(LSa + row * 8 + 4 * h);
       }
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
         const int row = wn * 64 + ni * 32 + l32;
-        scb[ni] = FMT == kMXFP8 ? (*reinterpret_cast<const uint32_t*>(LSb + row * 4) >> (8 * h))
+        scb[ni] = fp8_elems(FMT) ? (*reinterpret_cast<const uint32_t*>(LSb + row * 4) >> (8 * h))
                                 : *reinterpret_cast<const uint32_t*>(LSb + row * 8 + 4 * h);
       }
       auto frag = [&](const uint8_t* base, int row, int s) {
         const uint8_t* p = base + row * C::LDR;
         uint4 lo, hi = make_uint4(0, 0, 0, 0);
-        if (FMT == kMXFP8) {
+        if (fp8_elems(FMT)) {
           lo = *reinterpret_cast<const uint4*>(p + (2 * s) * 32 + 16 * h);
           hi = *reinterpret_cast<const uint4*>(p + (2 * s + 1) * 32 + 16 * h);
         } else {
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
       };
 #pragma unroll
       for (int s = 0; s < C::STEPS; ++s) {
-        const int sel = FMT == kMXFP8 ? 2 * s : s;    // scale byte of this lane's block
+        const int sel = fp8_elems(FMT) ? 2 * s : s;   // scale byte of this lane's block
         intx8 fa[4], fb[2];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) fa[mi] = frag(La, wm * 128 + mi * 32 + l32, s);
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
 
   // epilogue: alpha * acc -> BF16 (RNE).  Lane holds column m = l32 of D = C^T,
   // rows n = 8*(r/4) + 4*h + r%4 of each 32x32 tile.
-  const float alpha = 1.0f;
+  const float alpha = FMT == kFP8 ? fp8_s_dec(*a_amax) * fp8_s_dec(*b_amax) : 1.0f;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int64_t m = m0 + wm * 128 + mi * 32 + l32;
@@ -311,7 +314,7 @@ static_assert(kMxLds <= 160 * 1024, "MX staged LDS plan");
 // Stages per scale period: 16 bytes of a row hold 4 MXFP4 stages (128 K
 // each, 4 blocks) or 8 MXFP8 stages (64 K each, 2 blocks).
 template <int FMT>
-constexpr int mx_period() { return FMT == kMXFP8 ? 8 : 4; }
+constexpr int mx_period() { return fp8_elems(FMT) ? 8 : 4; }
 
 // Fragments and scale operands of one stage for one wave.  MXFP8: fa[0]/fa[1]
 // are bytes 0-15 / 16-31 of the operand (chunks h and 2 + h); MXFP4: fa[s] is
@@ -340,10 +343,13 @@ __device__ __forceinline__ void mx_read(MxFrag& F, const uint8_t* buf, const uin
   };
   if (Q < 8) {
     const int j = Q >> 2, mi = Q & 3, row = wm * 128 + mi * 32 + l32;
-    F.fa[j][mi] = chunk(La, row, FMT == kMXFP8 ? (j == 0 ? h : 2 + h) : 2 * h + j);
+    F.fa[j][mi] = chunk(La, row, fp8_elems(FMT) ? (j == 0 ? h : 2 + h) : 2 * h + j);
   } else if (Q < 12) {
     const int j = (Q - 8) >> 1, ni = (Q - 8) & 1, row = wn * 64 + ni * 32 + l32;
-    F.fb[j][ni] = chunk(Lb, row, FMT == kMXFP8 ? (j == 0 ? h : 2 + h) : 2 * h + j);
+    F.fb[j][ni] = chunk(Lb, row, fp8_elems(FMT) ? (j == 0 ? h : 2 + h) : 2 * h + j);
+  } else if (FMT == kFP8) {                        // per-tensor: E8M0 unit scale
+    if (Q < 16) F.sa[Q - 12] = 0x7Fu;
+    else F.sb[Q - 16] = 0x7Fu;
   } else if (Q < 16) {
     const int mi = Q - 12, row = wm * 128 + mi * 32 + l32;
     F.sa[mi] = FMT == kMXFP8 ? (uint32_t)Sa[row * 16 + sb0 + h]
@@ -359,13 +365,13 @@ __device__ __forceinline__ void mx_read(MxFrag& F, const uint8_t* buf, const uin
 // I / 8).
 template <int FMT, int I>
 __device__ __forceinline__ void mx_mfma(floatx16 (&acc)[4][2], const MxFrag& F) {
-  constexpr int FMTC = FMT == kMXFP8 ? 0 : 4;            // cbsz / blgp operand type
-  constexpr int s = FMT == kMXFP8 ? 0 : I >> 3;
+  constexpr int FMTC = fp8_elems(FMT) ? 0 : 4;           // cbsz / blgp operand type
+  constexpr int s = fp8_elems(FMT) ? 0 : I >> 3;
   constexpr int mi = (I & 7) >> 1, ni = I & 1;
   const u32x4 z = {0u, 0u, 0u, 0u};
   const u32x4 al = F.fa[s][mi], bl = F.fb[s][ni];
-  const u32x4 ah = FMT == kMXFP8 ? F.fa[1][mi] : z;
-  const u32x4 bh = FMT == kMXFP8 ? F.fb[1][ni] : z;
+  const u32x4 ah = fp8_elems(FMT) ? F.fa[1][mi] : z;
+  const u32x4 bh = fp8_elems(FMT) ? F.fb[1][ni] : z;
   const intx8 a = __builtin_bit_cast(intx8, __builtin_shufflevector(al, ah, 0, 1, 2, 3, 4, 5, 6, 7));
   const intx8 b = __builtin_bit_cast(intx8, __builtin_shufflevector(bl, bh, 0, 1, 2, 3, 4, 5, 6, 7));
   acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[mi][ni], FMTC, FMTC, s,
@@ -391,7 +397,11 @@ __device__ __forceinline__ void mx_mfma(floatx16 (&acc)[4][2], const MxFrag& F) 
 // barrier that precedes its first read on slot 2j - 1.  A scale period q is
 // issued with code stage q P on slot 2 q P - 7 into the buffer of period q - 2,
 // whose last read was on slot 2 q P - 2 P - 2 (P >= 4 stages per period).
-constexpr int kMxPpLoads = 5;                            // loads per issued stage per wave
+// Loads per issued stage per wave: four code loads and the scale slot (none
+// for per-tensor FP8).
+template <int FMT>
+constexpr int mx_pp_loads() { return FMT == kFP8 ? 4 : 5; }
+static_assert(kMxStages == 4, "the stage ring is indexed with s & 3");
 
 struct MxPpSrc {
   const uint8_t* codes;                                  // this group's operand
@@ -411,6 +421,7 @@ __device__ __forceinline__ void mx_pp_issue(const MxPpSrc& x, int64_t s, int lan
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     dma_to_lds<16>(x.codes + cs * kMxRowB, x.code_off[i], buf + i * 16 * kMxRowB);
+  if (FMT == kFP8) return;
   const int64_t q = s / PER, cq = q < x.NP ? q : x.NP - 1;
   if (s - q * PER == 0)
     dma_to_lds<16>(x.scales + cq * 16, x.scale_off, x.scale_lds + (uint32_t)(q & 1) * kMxScB);
@@ -469,7 +480,7 @@ __device__ __forceinline__ void mx_pp_read(MxFrag& F, const uint8_t* smem, int64
                                            int h, int l32) {
   constexpr int PER = mx_period<FMT>();
   const int64_t q = s / PER;
-  const int sb0 = (int)(s - q * PER) * (FMT == kMXFP8 ? 2 : 4);
+  const int sb0 = (int)(s - q * PER) * (fp8_elems(FMT) ? 2 : 4);
   mx_pp_read_from<FMT, 0>(F, smem + (s & 3) * kMxStageB, smem + kMxScOff + (q & 1) * kMxScB, sb0,
                           wm, wn, h, l32);
 }
@@ -477,8 +488,9 @@ __device__ __forceinline__ void mx_pp_read(MxFrag& F, const uint8_t* smem, int64
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_gemm_mx_pp(
     int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
-    const uint8_t* b_codes, const uint8_t* b_scales, uint16_t* __restrict__ c, int64_t ldc,
-    int tiles_m, int tiles_n, int vec_store) {
+    const float* __restrict__ a_amax, const uint8_t* b_codes, const uint8_t* b_scales,
+    const float* __restrict__ b_amax, uint16_t* __restrict__ c, int64_t ldc, int tiles_m,
+    int tiles_n, int vec_store) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -489,13 +501,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx_pp(
   // group and wave within the group, scalar: they address the direct loads
   const int gs = __builtin_amdgcn_readfirstlane(wave >> 2);
   const int w = __builtin_amdgcn_readfirstlane(wave & 3);
-  const int64_t code_ld = FMT == kMXFP8 ? K : K / 2, scale_ld = K / 32;
+  const int64_t code_ld = fp8_elems(FMT) ? K : K / 2, scale_ld = K / 32;
   const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
   MxPpSrc x;
   x.codes = gs == 0 ? a_codes : b_codes;
   x.scales = gs == 0 ? a_scales : b_scales;
-  x.KT = code_ld / kMxRowB;                              // a multiple of 4 (K % 512 == 0)
-  x.NP = x.KT / mx_period<FMT>();
+  x.KT = code_ld / kMxRowB;
+  x.NP = x.KT / mx_period<FMT>();                        // scale periods (none for per-tensor FP8)
   {
     const int64_t base = gs == 0 ? m0 : n0, rows = gs == 0 ? M : N;
 #pragma unroll
@@ -523,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx_pp(
   mx_pp_issue<FMT>(x, 1, lane);
   mx_pp_issue<FMT>(x, 2, lane);
   mx_pp_issue<FMT>(x, 3, lane);
-  wait_vmcnt<3 * kMxPpLoads>();                          // stage 0 and period 0 in
+  wait_vmcnt<3 * mx_pp_loads<FMT>()>();                  // stage 0 and period 0 in
   lds_barrier();
   MxFrag F;
   if (gs == 0) {
@@ -532,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx_pp(
       pin_frag(F);
       mx_pp_mfmas<FMT>(acc, F);                          // slot 2j
       pin_acc(acc);
-      wait_vmcnt<2 * kMxPpLoads>();                      // stage j + 1 in
+      wait_vmcnt<2 * mx_pp_loads<FMT>()>();              // stage j + 1 in
       lds_barrier();
       mx_pp_read<FMT>(F, smem, j + 1, wm, wn, h, l32);   // slot 2j + 1
       mx_pp_issue<FMT>(x, j + 4, lane);
@@ -541,7 +553,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx_pp(
   } else {
     for (int64_t j = 0; j < x.KT; ++j) {
       mx_pp_read<FMT>(F, smem, j, wm, wn, h, l32);       // slot 2j
-      wait_vmcnt<2 * kMxPpLoads>();                      // stage j + 1 in
+      wait_vmcnt<2 * mx_pp_loads<FMT>()>();              // stage j + 1 in
       lds_barrier();
       pin_frag(F);
       mx_pp_issue<FMT>(x, j + 4, lane);                  // slot 2j + 1
@@ -552,7 +564,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx_pp(
   }
   wait_vmcnt<0>();                                       // the clamped tail loads land in LDS the epilogue reuses
   lds_barrier();
-  store_tile_bf16(acc, smem, 1.0f, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
+  const float alpha = FMT == kFP8 ? fp8_s_dec(*a_amax) * fp8_s_dec(*b_amax) : 1.0f;
+  store_tile_bf16(acc, smem, alpha, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
 }
 
 template <int FMT>
@@ -562,7 +575,7 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   using C = Cfg<FMT>;
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
   const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  const int64_t code_ld = FMT == kMXFP8 ? K : K / 2;
+  const int64_t code_ld = fp8_elems(FMT) ? K : K / 2;
   const int64_t scale_ld = FMT == kNVFP4 ? K / 16 : K / 32;
   const bool fast = (K % C::BK == 0) && al16(ac) && al16(bc) && (code_ld % 16 == 0) &&
                     ((scale_ld * 1) % C::SB == 0) &&
@@ -583,7 +596,9 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   // staged kernel: whole 64-byte code segments per stage, 16-byte scale pieces
   // per scale period (K % 512 == 0 for both formats), 32-bit byte offsets
   // within each operand
-  const bool staged = K > 0 && K % 512 == 0 && al16(ac) && al16(bc) && al16(as) && al16(bs) &&
+  // (per-tensor FP8: 64-byte stages only, no scale periods and no scale arrays)
+  const bool staged = K > 0 && (FMT == kFP8 ? K % 64 == 0 : K % 512 == 0) && al16(ac) && al16(bc) &&
+                      (FMT == kFP8 || (al16(as) && al16(bs))) &&
                       M * code_ld < ((int64_t)1 << 32) && N * code_ld < ((int64_t)1 << 32);
   static bool mx_attr_set = false;
   if (staged) {
@@ -593,8 +608,8 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
         return hipErrorInvalidConfiguration;
       mx_attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemm_mx_pp<FMT>), grid, block, kMxLds, s, M, N, K, ac, as, bc, bs, cp, ldc,
-                       tiles_m, tiles_n, vec_store ? 1 : 0);
+    hipLaunchKernelGGL((k_gemm_mx_pp<FMT>), grid, block, kMxLds, s, M, N, K, ac, as, aa, bc, bs, ba,
+                       cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
     return hipGetLastError();
   }
   if (fast)
@@ -619,6 +634,9 @@ hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* 
     case kMXFP4:
       return launch_gemm_t<kMXFP4>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax,
                                    c, ldc, s);
+    case kFP8:
+      return launch_gemm_t<kFP8>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax, c,
+                                 ldc, s);
     default:
       return launch_gemm_t<kMXFP8>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax,
                                    c, ldc, s);

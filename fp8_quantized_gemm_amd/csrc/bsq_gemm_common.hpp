@@ -69,6 +69,12 @@ __device__ __forceinline__ float nvfp4_s_dec(float amax) {
   return 1.0f / s_enc;
 }
 
+// Per-tensor FP8 decode scale: 1 / (448 / amax), 1 for amax == 0.
+__device__ __forceinline__ float fp8_s_dec(float amax) {
+  const float s_enc = amax == 0.0f ? 1.0f : fminf(448.0f / amax, 3.40282346638528859812e+38f);
+  return 1.0f / s_enc;
+}
+
 // Output tile of block `pid`.  Workgroups are dealt round-robin to the 8 XCDs
 // (each with its own L2), so block pid runs on XCD pid % 8; the remap gives
 // every XCD one contiguous run of the tile order, and the tile order sweeps

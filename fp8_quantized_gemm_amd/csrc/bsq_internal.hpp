@@ -6,7 +6,10 @@
 
 namespace bsq {
 
-enum Fmt { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2 };
+enum Fmt { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2, kFP8 = 3 };   // kFP8: per-tensor E4M3
+
+// One-byte (E4M3) elements: MXFP8 and per-tensor FP8.
+constexpr bool fp8_elems(int f) { return f == kMXFP8 || f == kFP8; }
 
 // Sets *a = 0 and *b = 0 (either may be null).
 hipError_t launch_zero_amax(float* a, float* b, hipStream_t s);
@@ -37,6 +40,11 @@ hipError_t launch_quant_tile(Fmt fmt, bool sr, bool rht_col, bool two_d, const v
                              uint64_t seed, uint32_t offset, uint8_t* codes_row,
                              uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                              hipStream_t s);
+
+// Per-tensor FP8 codes of x [R, C] (codes_row [R, C]) and of x^T (codes_col
+// [C, R]), either may be null, under the already reduced *amax.
+hipError_t launch_fp8_qt(const void* x, int64_t R, int64_t C, const float* amax,
+                         uint8_t* codes_row, uint8_t* codes_col, hipStream_t s);
 
 // NVFP4 GEMM (exact FP16 dequant + FP16 MFMA).
 hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,

@@ -683,6 +683,119 @@ __global__ __launch_bounds__(kQtThreads) void k_qt_nvfp4(
   }
 }
 
+// ---------------------------------------------------------------- per-tensor FP8, row + column
+//
+// The FP8 baseline's operands: code = E4M3(x * s_enc), s_enc = 448 / amax.
+// The rule does not depend on the orientation, so the column output is the
+// row codes transposed.
+
+__device__ __forceinline__ float fp8_s_enc(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  return fminf(448.0f / amax, kFltMax);
+}
+
+// 4 x 4 byte transpose: rows a, b, c, d (4 bytes each) -> columns 0..3.
+__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                             uint32_t (&o)[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+  const uint32_t t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+  const uint32_t t2 = __builtin_amdgcn_perm(d, c, 0x05010400u);   // c0 d0 c1 d1
+  const uint32_t t3 = __builtin_amdgcn_perm(d, c, 0x07030602u);   // c2 d2 c3 d3
+  o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);              // a0 b0 c0 d0
+  o[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);              // a1 b1 c1 d1
+  o[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// One 512-thread workgroup per 256 x 256 tile (R and C multiples of 256).
+// Thread t owns columns 8 (t % 32) .. +8 of rows 16 (t / 32) .. +16.  Row
+// codes go straight out (32 lanes write one 256-byte row segment).  Column
+// codes are transposed in registers, staged in LDS (256 columns x 256 bytes,
+// 16-byte unit u of column c at unit u ^ ((c / 8) % 16), so the eight lanes
+// of a write phase hit distinct banks) and written as whole 256-byte
+// segments of the [C, R] output.
+__global__ __launch_bounds__(kQtThreads) void k_fp8_qt(const uint16_t* __restrict__ x, int64_t R,
+                                                       int64_t C, int tiles_r, int tiles_c,
+                                                       const float* __restrict__ amax,
+                                                       uint8_t* __restrict__ codes_row,
+                                                       uint8_t* __restrict__ codes_col) {
+  __shared__ __attribute__((aligned(16))) uint8_t col_codes[kQtTile * kQtTile];
+  int tr, tc;
+  qt_tile_of_block(blockIdx.x, tiles_r, tiles_c, tr, tc);
+  const int t = threadIdx.x, cg = t & 31, rb = t >> 5;
+  const int64_t r0 = (int64_t)tr * kQtTile + rb * 16, c0 = (int64_t)tc * kQtTile + cg * 8;
+
+  uint4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * C + c0);
+  const float s_enc = fp8_s_enc(*amax);
+
+  uint2 code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float y[8];
+    unpack8(v[i], y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = y[e] * s_enc;
+    code[i] = encode8_fp8(y);
+    if (codes_row) *reinterpret_cast<uint2*>(codes_row + (r0 + i) * C + c0) = code[i];
+  }
+  if (!codes_col) return;
+
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {           // columns 4 half .. 4 half + 3
+    uint32_t col[4][4];                              // [column][row group of 4]
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t o[4];
+      const int i = 4 * g;
+      if (half == 0) transpose4x4(code[i].x, code[i + 1].x, code[i + 2].x, code[i + 3].x, o);
+      else transpose4x4(code[i].y, code[i + 1].y, code[i + 2].y, code[i + 3].y, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) col[j][g] = o[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cl = cg * 8 + 4 * half + j;
+      *reinterpret_cast<uint4*>(col_codes + cl * kQtTile + ((rb ^ (cg & 15)) << 4)) =
+          make_uint4(col[j][0], col[j][1], col[j][2], col[j][3]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int q = t + kQtThreads * k;
+    const int cl = q >> 4, u = q & 15;
+    const uint4 val = *reinterpret_cast<const uint4*>(col_codes + cl * kQtTile + ((u ^ ((cl >> 3) & 15)) << 4));
+    *reinterpret_cast<uint4*>(codes_col + ((int64_t)tc * kQtTile + cl) * R + (int64_t)tr * kQtTile + u * 16) = val;
+  }
+}
+
+// Any R, C multiples of 16: one 8-element row chunk per lane (grid-stride);
+// column codes are stored byte by byte.
+__global__ __launch_bounds__(256) void k_fp8_qt_flat(const uint4* __restrict__ x, int64_t R,
+                                                     int64_t C, const float* __restrict__ amax,
+                                                     uint8_t* __restrict__ codes_row,
+                                                     uint8_t* __restrict__ codes_col) {
+  const float s_enc = fp8_s_enc(*amax);
+  const int64_t nchunk = R * C / 8;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nchunk;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    float y[8];
+    unpack8(x[q], y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = y[e] * s_enc;
+    const uint2 code = encode8_fp8(y);
+    if (codes_row) reinterpret_cast<uint2*>(codes_row)[q] = code;
+    if (codes_col) {
+      const int64_t r = (q * 8) / C, c0 = (q * 8) % C;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        codes_col[(c0 + e) * R + r] = (uint8_t)((e < 4 ? code.x : code.y) >> (8 * (e & 3)));
+    }
+  }
+}
+
 // Row-blocks per lane: as many as keeps >= 4096 waves in flight (up to 16).
 int pick_rbs(int64_t nrowblocks, int64_t waves_x) {
   int rbs = 16;
@@ -756,6 +869,26 @@ hipError_t launch_quant_flat(Fmt fmt, bool sr, bool rht, const void* x, int64_t 
     BSQ_FLAT(kMXFP8, false, false);
   }
 #undef BSQ_FLAT
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_qt(const void* x, int64_t R, int64_t C, const float* amax,
+                         uint8_t* codes_row, uint8_t* codes_col, hipStream_t s) {
+  const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (R % kQtTile == 0 && C % kQtTile == 0 && R > 0 && C > 0 && al16(x) &&
+      (!codes_row || al16(codes_row)) && (!codes_col || al16(codes_col)) &&
+      (R / kQtTile) * (C / kQtTile) < (int64_t)1 << 31) {
+    const int tiles_r = (int)(R / kQtTile), tiles_c = (int)(C / kQtTile);
+    hipLaunchKernelGGL(k_fp8_qt, dim3((unsigned)(tiles_r * tiles_c)), dim3(kQtThreads), 0, s,
+                       static_cast<const uint16_t*>(x), R, C, tiles_r, tiles_c, amax, codes_row,
+                       codes_col);
+    return hipGetLastError();
+  }
+  const int64_t nchunk = R * C / 8;
+  int64_t g = (nchunk + 255) / 256;
+  g = g < 1 ? 1 : (g > 256 * 32 ? 256 * 32 : g);
+  hipLaunchKernelGGL(k_fp8_qt_flat, dim3((unsigned)g), dim3(256), 0, s,
+                     static_cast<const uint4*>(x), R, C, amax, codes_row, codes_col);
   return hipGetLastError();
 }
 

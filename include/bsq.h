@@ -15,6 +15,10 @@
  *  - HN page opcode84 (Triton on Blackwell quote, OCP MX spec link): MXFP8
  *    (E4M3 elements) and MXFP4 (E2M1 elements) with one E8M0 power-of-two
  *    scale per 32 elements, applied inside the matrix unit.
+ *  - NVFP4 pretraining post, the paragraph after the example script (the FP8
+ *    baseline run, quantization=te_fp8_delayedscaling) and section
+ *    "Performance results" (Table 1, Figure 2: NVFP4 against that FP8
+ *    baseline): the per-tensor FP8 format BSQ_FP8 below.
  *
  * Numerical definitions (bit-exact contract of the quantizers):
  *  - E2M1 magnitudes {0,0.5,1,1.5,2,3,4,6}, ties to the even code, saturate
@@ -26,6 +30,11 @@
  *    s_dec = 1/s_enc.  Block: sf = (a_b/6)*s_enc; S = E4M3(sf);
  *    enc = S ? min(s_enc/S, FLT_MAX) : 0; code = E2M1(x*enc).  FP32 IEEE
  *    RNE at every step, no fused multiply-add.
+ *  - Per-tensor FP8 (BSQ_FP8): amax = max|x|; s_enc = 448/amax (FP32; 1 if
+ *    amax == 0; <= FLT_MAX); s_dec = 1/s_enc; code = E4M3(x*s_enc), signed,
+ *    RNE, saturating at 448.  No block scales; the column output is the same
+ *    rule on x^T (the row codes transposed).  The delayed-scaling amax history
+ *    of the baseline recipe spans training steps and is not modelled.
  *  - MX scale: e = floor(log2 a_b) - emax (emax 2 for E2M1, 8 for E4M3),
  *    -127 for an all-zero block, clamped to [-127,127], stored as e+127;
  *    element = E2M1/E4M3(x * 2^-e).
@@ -71,7 +80,9 @@ typedef enum {
   BSQ_EHIP = 3           /* HIP launch error */
 } bsq_status;
 
-typedef enum { BSQ_NVFP4 = 0, BSQ_MXFP4 = 1, BSQ_MXFP8 = 2 } bsq_format;
+/* BSQ_FP8: per-tensor FP8, accepted by fp8_quantize_transpose (implied) and
+ * bs_gemm only; the other quantizers return BSQ_EUNSUPPORTED for it. */
+typedef enum { BSQ_NVFP4 = 0, BSQ_MXFP4 = 1, BSQ_MXFP8 = 2, BSQ_FP8 = 3 } bsq_format;
 typedef enum { BSQ_RNE = 0, BSQ_SR = 1 } bsq_rounding;
 
 /*
@@ -143,6 +154,20 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
                               void* stream);
 
 /*
+ * Per-tensor FP8 (E4M3) of x[rows, cols] (BF16) in both orientations from
+ * one amax pass and one encode pass: the FP8 baseline's operands for FPROP
+ * (rowwise), DGRAD (W columnwise) and WGRAD (dY and X columnwise).
+ *   codes_row : out, uint8 [rows, cols], E4M3 codes of x (or NULL).
+ *   codes_col : out, uint8 [cols, rows], E4M3 codes of x^T, i.e. codes_row
+ *               transposed (or NULL; not both NULL).
+ *   amax      : out, device FP32 scalar max|x| (the reduction's accumulator;
+ *               required).  The GEMM derives s_dec from it.
+ * Requires rows % 16 == 0 and cols % 16 == 0.
+ */
+bsq_status fp8_quantize_transpose(const void* x, int64_t rows, int64_t cols, uint8_t* codes_row,
+                                  uint8_t* codes_col, float* amax, void* stream);
+
+/*
  * C[M, N] (BF16, row-major, row stride ldc >= N elements) =
  *     alpha * sum_k deq(A)[m, k] * deq(B)[n, k]
  * with A [M, K] and B [N, K] both K-major (quantized along K), FP32
@@ -155,6 +180,10 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
  *   MXFP4: codes [M, K/2], MXFP8: codes [M, K]; E8M0 scales [M, K/32];
  *          a_amax and b_amax are ignored (may be NULL); alpha = 1.
  *          Requires K % 32 == 0.
+ *   FP8:   per-tensor E4M3 codes [M, K] (fp8_quantize_transpose); a_scales
+ *          and b_scales are ignored (may be NULL); device FP32 a_amax and
+ *          b_amax required; alpha = s_dec(a_amax) * s_dec(b_amax) with
+ *          s_dec = 1/(448/amax).  Requires K % 32 == 0.
  * M and N may be any value >= 0.  C must not alias any input.
  */
 bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K,

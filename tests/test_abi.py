@@ -101,6 +101,22 @@ def test_quantize_transpose_argument_errors():
                                 None, None, None, None) == bsq.BSQ_EINVAL
 
 
+def _fp8(rows=32, cols=32, x=FAKE, row=FAKE, col=FAKE, amax=FAKE):
+    return bsq.lib().fp8_quantize_transpose(x, rows, cols, row, col, amax, None)
+
+
+def test_fp8_quantize_transpose_argument_errors():
+    assert _fp8(rows=24) == bsq.BSQ_EINVAL                # rows % 16
+    assert _fp8(cols=40) == bsq.BSQ_EINVAL                # cols % 16
+    assert _fp8(row=None, col=None) == bsq.BSQ_EINVAL     # no output
+    assert _fp8(amax=None) == bsq.BSQ_EINVAL              # amax is required
+    assert _fp8(amax=FAKE + 2) == bsq.BSQ_EINVAL          # misaligned amax
+    assert _fp8(x=None) == bsq.BSQ_EINVAL
+    assert _fp8(row=FAKE + 8) == bsq.BSQ_EINVAL           # misaligned codes
+    assert _mx(fmt=3) == bsq.BSQ_EUNSUPPORTED             # not an MX format
+    assert _qt(fmt=3) == bsq.BSQ_EUNSUPPORTED             # per-tensor FP8 has its own entry point
+
+
 def test_bs_gemm_argument_errors():
     L = bsq.lib()
     g = lambda fmt=0, M=16, N=16, K=32, ldc=16, a=FAKE, amax=FAKE, c=FAKE: L.bs_gemm(
@@ -113,6 +129,12 @@ def test_bs_gemm_argument_errors():
     assert g(c=None) == bsq.BSQ_EINVAL
     assert g(fmt=9) == bsq.BSQ_EINVAL
     assert g(M=0) == bsq.BSQ_OK and g(N=0) == bsq.BSQ_OK  # empty output: nothing to launch
+    # per-tensor FP8: scales may be NULL, both amaxes are required
+    f = lambda K=64, amax=FAKE, sc=None: L.bs_gemm(3, 16, 16, K, FAKE, sc, amax, FAKE, sc, amax,
+                                                     FAKE, 16, None)
+    assert f(K=48) == bsq.BSQ_EINVAL                      # K % 32
+    assert f(amax=None) == bsq.BSQ_EINVAL
+    assert L.bs_gemm(1, 16, 16, 64, FAKE, None, None, FAKE, None, None, FAKE, 16, None) == bsq.BSQ_EINVAL
 
 
 def test_binding_raises_without_library(monkeypatch):
