@@ -13,12 +13,14 @@ One step = the whole hot path of one transformer-MLP layer on one GPU's share
 value = sum(2 M N K) / step time, with BF16 inputs already resident in HBM.
 
 The same step is then timed with the RHT setting flipped (reported as rht_off
-or rht_on), and the MX square workload (4096^3, MXFP8 and MXFP4: mx_quantize of
-both operands + GEMM) is timed on its own and reported with its roofline
-fraction.
+or rht_on); the same step with the per-tensor FP8 baseline the NVFP4 post
+compares against (fp8_baseline: E4M3 under 448 / amax, FP8 matrix path, and
+the NVFP4 step's speed relative to it); and the MX square workload (4096^3,
+MXFP8 and MXFP4: mx_quantize of both operands + GEMM) on its own, with its
+roofline fraction.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--no-rht]
-[--workload 8b|405b] [--no-cpu-baseline] [--no-mx].
+[--workload 8b|405b] [--no-cpu-baseline] [--no-mx] [--no-fp8].
 """
 
 import argparse
@@ -41,7 +43,7 @@ PEAK_FP8_TFLOPS = 5033.2       # dense FP8 MFMA (MXFP8 GEMM)
 PEAK_FP4_TFLOPS = 10066.3      # dense FP4 MFMA (MXFP4 GEMM)
 PEAK_HBM_GBS = 8000.0
 
-NV, MXF4, MXF8 = 0, 1, 2
+NV, MXF4, MXF8, FP8 = 0, 1, 2, 3
 RNE, SR = 0, 1
 
 
@@ -136,6 +138,79 @@ class Step:
         timed("q_dY_gu", lambda: self.quant("dY_gu", SR, self.rht))
         timed("DGRAD_gu", lambda: self.gemm(G["DGRAD_gu"]))
         timed("WGRAD_gu", lambda: self.gemm(G["WGRAD_gu"]))
+
+
+class Fp8Step:
+    """The same MLP-layer step with the per-tensor FP8 baseline the NVFP4 post
+    compares against (section "Performance results"): every tensor quantized
+    by fp8_quantize_transpose (E4M3 codes of x and x^T under 448 / amax), the
+    six GEMMs on the FP8 matrix path.  Shares the BF16 inputs of `step`."""
+
+    def __init__(self, step):
+        self.step = step
+        dev = step.dev
+        u8 = lambda *s_: torch.empty(s_, dtype=torch.uint8, device=dev)
+        self.q = {}
+        for name, x in step.t.items():
+            R, C = x.shape
+            self.q[name] = dict(rc=u8(R, C), cc=u8(C, R),
+                                ra=torch.empty(1, dtype=torch.float32, device=dev))
+
+    def quant(self, name):
+        x, b, st = self.step.t[name], self.q[name], self.step
+        R, C = x.shape
+        r = st.lib.fp8_quantize_transpose(P(x), R, C, P(b["rc"]), P(b["cc"]), P(b["ra"]), st.stream)
+        assert r == 0, (name, bsq.status_string(r))
+
+    def gemm(self, g):
+        name, (an, ao), (bn, bo), M, N, K = g
+        st = self.step
+        a, b = self.q[an], self.q[bn]
+        c = st.out[st.gemm_out[name]]
+        r = st.lib.bs_gemm(FP8, M, N, K, P(a[ao + "c"]), None, P(a["ra"]), P(b[bo + "c"]), None,
+                           P(b["ra"]), P(c), N, st.stream)
+        assert r == 0, (name, bsq.status_string(r))
+
+    def run(self, events=None):
+        G = {g[0]: g for g in self.step.gemms}
+        order = ["q:X", "q:W_gu", "FPROP_gu", "q:H", "q:W_down", "FPROP_down", "q:dY_down",
+                 "DGRAD_down", "WGRAD_down", "q:dY_gu", "DGRAD_gu", "WGRAD_gu"]
+        for item in order:
+            fn = (lambda n=item[2:]: self.quant(n)) if item.startswith("q:") else (lambda n=item: self.gemm(G[n]))
+            if events is None:
+                fn()
+                continue
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            events.setdefault(item, []).append((e0, e1))
+
+
+def fp8_baseline(step, steps, warmup, nvfp4_ms):
+    """Times Fp8Step like the NVFP4 step; reports its rate and the NVFP4 step's
+    speed relative to it (the pages' metric: NVFP4 over FP8 step throughput)."""
+    f = Fp8Step(step)
+    for _ in range(max(1, warmup)):
+        f.run()
+    torch.cuda.synchronize()
+    ev = {}
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        f.run(ev)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    per = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in ev.items()}
+    gemm_ms = sum(per[g[0]] for g in step.gemms)
+    return {"format": "per-tensor FP8 (E4M3, s = 448/amax) on the FP8 MFMA",
+            "ms_per_step": round(ms, 4),
+            "value": round(step.flops / (ms * 1e-3) / 1e12, 2),
+            "gemm_tflops": round(step.flops / (gemm_ms * 1e-3) / 1e12, 1),
+            "gemm_frac_of_fp8_peak": round(step.flops / (gemm_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "quant_ms": round(sum(v for k, v in per.items() if k.startswith("q:")), 4),
+            "nvfp4_speedup_over_fp8": round(ms / nvfp4_ms, 4)}
 
 
 def mx_square(device, reps=20):
@@ -252,6 +327,7 @@ def main():
     ap.add_argument("--no-rht", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MX square-GEMM lines")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the per-tensor FP8 baseline step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path "
@@ -337,6 +413,8 @@ def main():
             "value": round(step.flops / (ms_other * 1e-3) / 1e12, 2)},
         "wall_s": round(wall, 3),
     }
+    if not args.no_fp8:
+        out["fp8_baseline"] = fp8_baseline(step, args.steps, args.warmup, ms)
     if not args.no_mx:
         out["mx_square_4096"] = mx_square(dev)
     if not args.no_cpu_baseline:
