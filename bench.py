@@ -13,7 +13,9 @@ One step = the whole hot path of one transformer-MLP layer on one GPU's share
 value = sum(2 M N K) / step time, with BF16 inputs already resident in HBM.
 
 The same step is then timed with the RHT setting flipped (reported as rht_off
-or rht_on); the same step with the per-tensor FP8 baseline the NVFP4 post
+or rht_on); the WGRAD_down error with and without the RHT is measured against
+an FP64 product (rht_wgrad_error, 8B only); the same step with the per-tensor
+FP8 baseline the NVFP4 post
 compares against (fp8_baseline: E4M3 under 448 / amax, FP8 matrix path, and
 the NVFP4 step's speed relative to it); and the MX square workload (4096^3,
 MXFP8 and MXFP4: mx_quantize of both operands + GEMM) on its own, with its
@@ -185,6 +187,31 @@ class Fp8Step:
             fn()
             e1.record()
             events.setdefault(item, []).append((e0, e1))
+
+
+def rht_wgrad_error(step):
+    """Accuracy side of the recipe's RHT (WGRAD inputs only): relative
+    Frobenius error of the NVFP4 WGRAD_down output dW = dY_down^T . H against
+    the FP64 product of the same BF16 inputs, with the column RHT on and off
+    (dY_down: SR; H: RNE, N(0,1) with 0.1% x50 outliers)."""
+    g = {x[0]: x for x in step.gemms}["WGRAD_down"]
+    dY, Hm = step.t["dY_down"], step.t["H"]
+    ref = dY.double().t() @ Hm.double()
+    nref = float(torch.linalg.norm(ref))
+    out = {}
+    saved = step.rht
+    for flag, key in ((1, "rht_on"), (0, "rht_off")):
+        step.rht = flag
+        step.quant("dY_down", SR, flag)
+        step.quant("H", RNE, flag)
+        step.gemm(g)
+        torch.cuda.synchronize()
+        c = step.out[step.gemm_out["WGRAD_down"]].double()
+        out[key] = float(torch.linalg.norm(c - ref)) / nref
+    step.rht = saved
+    del ref
+    out["error_ratio_on_over_off"] = out["rht_on"] / out["rht_off"]
+    return {k: round(v, 6) for k, v in out.items()}
 
 
 def fp8_baseline(step, steps, warmup, nvfp4_ms):
@@ -415,6 +442,8 @@ def main():
     }
     if not args.no_fp8:
         out["fp8_baseline"] = fp8_baseline(step, args.steps, args.warmup, ms)
+    if args.workload == "8b":
+        out["rht_wgrad_error"] = rht_wgrad_error(step)
     if not args.no_mx:
         out["mx_square_4096"] = mx_square(dev)
     if not args.no_cpu_baseline:
