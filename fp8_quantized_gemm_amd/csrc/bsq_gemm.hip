@@ -391,7 +391,8 @@ __device__ __forceinline__ void mx_mfma(floatx16 (&acc)[4][2], const MxFrag& F) 
 // the A rows and group 1 the B rows (wave w: rows 64 w .. 64 w + 63, four
 // direct loads of 16 rows x 64 bytes), each with one scale load (the rows'
 // 16 bytes of a scale period at the period's first stage, else lane 0
-// reloading its own 16 bytes in place) so that every issue is five loads.
+// reloading its own 16 bytes in place) so that every issue is five loads
+// (four for per-tensor FP8, which has no scales).
 // Stage j is issued on slot 2j - 7 and waited for by its issuing waves on slot
 // 2j - 2 (their loads of stages j + 1 and j + 2 may stay in flight), before the
 // barrier that precedes its first read on slot 2j - 1.  A scale period q is

@@ -71,6 +71,24 @@ def test_fp8_gemm(M, N, K):
     _check(C, G.gemm_fp8(ra["row_codes"], ra["amax"], rb["row_codes"], rb["amax"]), f"fp8 {M}x{N}x{K}")
 
 
+def test_fp8_zero_tensor_and_empty_k():
+    """All-zero input: amax 0, s_enc 1, all codes 0 (the oracle agrees); a GEMM
+    with K = 0 writes zeros."""
+    announce("fp8 zero / K=0")
+    x = torch.zeros((256, 256), dtype=torch.bfloat16, device="cuda")
+    d = bsq.fp8_quantize_transpose(x)
+    torch.cuda.synchronize()
+    ref = Q.fp8_quantize_transpose(bits(x))
+    assert f32(d["amax"])[0] == 0.0 == ref["amax"]
+    assert_bytes_equal(u8(d["row_codes"]), ref["row_codes"], "row codes")
+    assert not u8(d["col_codes"]).any()
+    c0 = torch.full((32, 48), 3.0, dtype=torch.bfloat16, device="cuda")
+    codes = torch.zeros((48, 0), dtype=torch.uint8, device="cuda")
+    out = bsq.bs_gemm("fp8", codes[:32], None, codes, None, d["amax"], d["amax"], K=0, out=c0)
+    torch.cuda.synchronize()
+    assert not out.float().any()
+
+
 def test_fp8_wgrad_from_column_outputs():
     """WGRAD-shaped use: both operands from the column (x^T) outputs."""
     announce("fp8 wgrad")
