@@ -1,0 +1,37 @@
+"""SwiGLU of the MLP whose GEMMs the workloads model.
+
+Test infrastructure only (see oracle/__init__.py).
+
+The NVFP4 post's "Performance results" measure Llama 3 8B and Llama 3.1 405B;
+their MLP is gate/up projection -> SwiGLU -> down projection, so the BF16
+input H of the down projection (and of its WGRAD) is SwiGLU of the fused
+gate/up GEMM output.  The pages give no formula.  Readings:
+* [G | U] = Y_gu [T, 2F]: the first F columns are the gate, the last F the up
+  projection;
+* H = silu(G) * U with silu(g) = g / (1 + exp(-g)), evaluated in float64 on
+  the BF16 inputs and rounded once to BF16 (round to nearest even).
+"""
+
+import numpy as np
+
+from . import formats as F
+
+
+def silu_f64(g):
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def f64_to_bf16_bits(x):
+    """float64 -> BF16 bit patterns (uint16), round to nearest even."""
+    v = F.f64_to_bf16_rne(x).astype(np.float32)            # exact: BF16 values are FP32 values
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def swiglu(y_gu):
+    """H [T, F] BF16 bits from Y_gu [T, 2F] BF16 bits."""
+    y = F.bf16_bits_to_f32(y_gu).astype(np.float64)
+    T, F2 = y.shape
+    assert F2 % 2 == 0
+    Fh = F2 // 2
+    return f64_to_bf16_bits(silu_f64(y[:, :Fh]) * y[:, Fh:])
