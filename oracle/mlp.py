@@ -10,6 +10,11 @@ gate/up GEMM output.  The pages give no formula.  Readings:
   projection;
 * H = silu(G) * U with silu(g) = g / (1 + exp(-g)), evaluated in float64 on
   the BF16 inputs and rounded once to BF16 (round to nearest even).
+* Backward (the chain rule of H = silu(G) * U, nothing the pages add): from
+  the BF16 gradient dH [T, F], dG = dH * U * silu'(G) and dU = dH * silu(G),
+  silu'(g) = sigma(g) * (1 + g * (1 - sigma(g))), sigma the logistic
+  function; each output is evaluated in float64 and rounded once to BF16, and
+  dY_gu = [dG | dU] [T, 2F] keeps the forward's column order.
 """
 
 import numpy as np
@@ -35,3 +40,27 @@ def swiglu(y_gu):
     assert F2 % 2 == 0
     Fh = F2 // 2
     return f64_to_bf16_bits(silu_f64(y[:, :Fh]) * y[:, Fh:])
+
+
+def sigmoid_f64(g):
+    g = np.asarray(g, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-g))
+
+
+def dsilu_f64(g):
+    """d silu / d g = sigma(g) * (1 + g * (1 - sigma(g)))."""
+    g = np.asarray(g, dtype=np.float64)
+    s = sigmoid_f64(g)
+    return s * (1.0 + g * (1.0 - s))
+
+
+def swiglu_backward(y_gu, d_h):
+    """dY_gu [T, 2F] BF16 bits from Y_gu [T, 2F] and dH [T, F] BF16 bits."""
+    y = F.bf16_bits_to_f32(y_gu).astype(np.float64)
+    dh = F.bf16_bits_to_f32(d_h).astype(np.float64)
+    T, F2 = y.shape
+    Fh = F2 // 2
+    assert F2 % 2 == 0 and dh.shape == (T, Fh)
+    g, u = y[:, :Fh], y[:, Fh:]
+    return np.concatenate([f64_to_bf16_bits(dh * u * dsilu_f64(g)),
+                           f64_to_bf16_bits(dh * silu_f64(g))], axis=1)

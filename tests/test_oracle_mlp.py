@@ -5,6 +5,10 @@
 * The final BF16 rounding agrees with torch's float32 -> bfloat16 cast (RNE)
   on float32 inputs, and rounds float64 halfway cases to even.
 * H = silu(G) * U on a small case equals an independent scalar evaluation.
+* Backward: silu' agrees with torch autograd's float64 derivative of SiLU
+  and with a central finite difference of silu; dY_gu agrees with autograd's
+  vector-Jacobian product of silu(G) * U (rounded once to BF16), keeps the
+  [dG | dU] order, and reduces to dG = dH * U / 2, dU = 0 at G = 0.
 """
 
 import math
@@ -52,3 +56,39 @@ def test_swiglu_small_case_scalar():
             want = M.f64_to_bf16_bits(np.array([exact]))[0]
             assert h[t, j] == want, (t, j)
     assert not M.swiglu(_bits(np.concatenate([np.ones((2, 4)), np.zeros((2, 4))], axis=1))).view(np.int16).any()
+
+
+def test_dsilu_matches_autograd_and_finite_difference():
+    g = np.concatenate([np.linspace(-30, 30, 4001), np.random.default_rng(5).standard_normal(1000) * 5])
+    gt = torch.tensor(g, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.silu(gt).sum().backward()
+    np.testing.assert_allclose(M.dsilu_f64(g), gt.grad.numpy(), rtol=1e-13, atol=1e-15)
+    h = 1e-5
+    fd = (M.silu_f64(g + h) - M.silu_f64(g - h)) / (2 * h)
+    np.testing.assert_allclose(M.dsilu_f64(g), fd, rtol=1e-7, atol=1e-9)
+    assert M.dsilu_f64(np.array([0.0]))[0] == 0.5
+
+
+def test_swiglu_backward_matches_autograd_vjp():
+    rng = np.random.default_rng(6)
+    T, Fh = 7, 24
+    y = _bits(rng.standard_normal((T, 2 * Fh)) * 2)
+    dh = _bits(rng.standard_normal((T, Fh)) * 1e-3)
+    got = M.swiglu_backward(y, dh)
+    yt = torch.tensor(F.bf16_bits_to_f32(y).astype(np.float64), requires_grad=True)
+    dht = torch.tensor(F.bf16_bits_to_f32(dh).astype(np.float64))
+    (torch.nn.functional.silu(yt[:, :Fh]) * yt[:, Fh:]).backward(dht)
+    want = yt.grad.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # autograd's float64 result differs from the oracle's only in the last
+    # float64 bits, which decide the BF16 rounding with probability ~2^-44
+    np.testing.assert_array_equal(got, want)
+    assert got.shape == (T, 2 * Fh)
+
+
+def test_swiglu_backward_at_zero_gate():
+    u = np.array([[1.5, -2.0, 0.25, 3.0]])
+    y = _bits(np.concatenate([np.zeros((1, 4)), u], axis=1))
+    dh = _bits(np.array([[2.0, 0.5, -4.0, 1.0]]))
+    d = M.swiglu_backward(y, dh)
+    np.testing.assert_array_equal(F.bf16_bits_to_f32(d[:, :4]).astype(np.float64), [[1.5, -0.5, -0.5, 1.5]])
+    assert not (d[:, 4:] & 0x7FFF).any()
