@@ -17,12 +17,14 @@ or rht_on); the WGRAD_down error with and without the RHT is measured against
 an FP64 product (rht_wgrad_error, 8B only); the same step with the per-tensor
 FP8 baseline the NVFP4 post
 compares against (fp8_baseline: E4M3 under 448 / amax, FP8 matrix path, and
-the NVFP4 step's speed relative to it); and the MX square workload (4096^3,
+the NVFP4 step's speed relative to it); the SwiGLU forward and backward
+around the H and dY_gu quantizers, with and without their fused amaxes
+(swiglu_fused_quantize); and the MX square workload (4096^3,
 MXFP8 and MXFP4: mx_quantize of both operands + GEMM) on its own, with its
 roofline fraction.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--no-rht]
-[--workload 8b|405b] [--no-cpu-baseline] [--no-mx] [--no-fp8].
+[--workload 8b|405b] [--no-cpu-baseline] [--no-mx] [--no-fp8] [--no-swiglu].
 """
 
 import argparse
@@ -240,6 +242,80 @@ def fp8_baseline(step, steps, warmup, nvfp4_ms):
             "nvfp4_speedup_over_fp8": round(ms / nvfp4_ms, 4)}
 
 
+def swiglu_fused(step, reps=10):
+    """The producer-side fusion around the H and dY_gu quantizers: SwiGLU
+    forward of the step's Y_gu (FPROP_gu output) and backward with its dH
+    (DGRAD_down output), each followed by the NVFP4 quantize_transpose of its
+    output; unfused = SwiGLU alone, then quantize_transpose with its own amax
+    pass; fused = SwiGLU that also emits both amaxes, then
+    quantize_transpose_amax.  Median of `reps` timings per route (HIP events
+    on the launch stream); the SwiGLU kernels' own rate against the HBM peak
+    (algorithmic bytes: forward 6 B, backward 10 B per element of H)."""
+    lib, s, dev = step.lib, step.stream, step.dev
+    Y, dH = step.out["Y_gu"], step.out["dH"]
+    T, F2 = Y.shape
+    F = F2 // 2
+    H = torch.empty((T, F), dtype=torch.bfloat16, device=dev)
+    dY = torch.empty((T, F2), dtype=torch.bfloat16, device=dev)
+    am = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2)]
+    qh, qd = step.q["H"], step.q["dY_gu"]
+    rht, signs, seed = step.rht, step.signs, step.seed
+
+    def ok(st):
+        assert st == 0, bsq.status_string(st)
+
+    def fwd(amax):
+        ok(lib.swiglu_amax(P(Y), T, F, rht, signs, P(H), P(am[0]) if amax else None,
+                           P(am[1]) if amax else None, s))
+
+    def bwd(amax):
+        ok(lib.swiglu_backward_amax(P(Y), P(dH), T, F, rht, signs, P(dY), P(am[0]) if amax else None,
+                                    P(am[1]) if amax else None, s))
+
+    def qt(x, b, rnd):
+        R, C = x.shape
+        ok(lib.quantize_transpose(P(x), R, C, NV, 1, rnd, seed, 0, rht, signs, P(b["rc"]), P(b["rs"]),
+                                  P(b["ra"]), P(b["cc"]), P(b["cs"]), P(b["ca"]), s))
+
+    def qta(x, b, rnd):
+        R, C = x.shape
+        ok(lib.quantize_transpose_amax(P(x), R, C, 1, rnd, seed, 0, rht, signs, P(am[0]), P(am[1]),
+                                       P(b["rc"]), P(b["rs"]), P(b["cc"]), P(b["cs"]), s))
+
+    routes = {
+        "fwd_unfused": lambda: (fwd(False), qt(H, qh, RNE)),
+        "fwd_fused": lambda: (fwd(True), qta(H, qh, RNE)),
+        "bwd_unfused": lambda: (bwd(False), qt(dY, qd, SR)),
+        "bwd_fused": lambda: (bwd(True), qta(dY, qd, SR)),
+        "swiglu_fwd_amax": lambda: fwd(True),
+        "swiglu_bwd_amax": lambda: bwd(True),
+    }
+    res = {}
+    for name, fn in routes.items():
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        v = sorted(a.elapsed_time(b) for a, b in ts)
+        res[name] = v[len(v) // 2]
+    n = T * F
+    out = {"shape": {"tokens": T, "ffn": F}, "rht_col": bool(rht)}
+    for k in ("fwd", "bwd"):
+        out[k] = {"unfused_ms": round(res[k + "_unfused"], 4), "fused_ms": round(res[k + "_fused"], 4),
+                  "speedup": round(res[k + "_unfused"] / res[k + "_fused"], 4)}
+    for k, b in (("swiglu_fwd_amax", 6 * n), ("swiglu_bwd_amax", 10 * n)):
+        gbs = b / (res[k] * 1e-3) / 1e9
+        out[k] = {"ms": round(res[k], 4), "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del H, dY
+    return out
+
+
 def mx_square(device, reps=20):
     """The MX workload (4096 x 4096 x 4096, A and B N(0,1) with outliers):
     rowwise mx_quantize of both operands, then the block-scaled GEMM, for MXFP8
@@ -355,6 +431,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MX square-GEMM lines")
     ap.add_argument("--no-fp8", action="store_true", help="skip the per-tensor FP8 baseline step")
+    ap.add_argument("--no-swiglu", action="store_true", help="skip the fused SwiGLU + quantize lines")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path "
@@ -442,6 +519,8 @@ def main():
     }
     if not args.no_fp8:
         out["fp8_baseline"] = fp8_baseline(step, args.steps, args.warmup, ms)
+    if not args.no_swiglu:
+        out["swiglu_fused_quantize"] = swiglu_fused(step)
     if args.workload == "8b":
         out["rht_wgrad_error"] = rht_wgrad_error(step)
     if not args.no_mx:

@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_PKG, "libbsq.so")
 BSQ_OK, BSQ_EINVAL, BSQ_EUNSUPPORTED, BSQ_EHIP = 0, 1, 2, 3
 FORMATS = {"nvfp4": 0, "mxfp4": 1, "mxfp8": 2, "fp8": 3}
 ROUNDING = {"rne": 0, "sr": 1}
-ABI_SYMBOLS = ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "fp8_quantize_transpose",
-               "bs_gemm", "bsq_status_string")
+ABI_SYMBOLS = ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "quantize_transpose_amax",
+               "fp8_quantize_transpose", "swiglu_amax", "swiglu_backward_amax", "bs_gemm",
+               "bsq_status_string")
 
 
 class BsqError(RuntimeError):
@@ -46,10 +47,13 @@ def lib():
         L.mx_quantize.argtypes = [P, I64, I64, I, I, U64, U32, P, P, P]
         L.quantize_transpose.argtypes = [P, I64, I64, I, I, I, U64, U32, I, U16,
                                          P, P, P, P, P, P, P]
+        L.quantize_transpose_amax.argtypes = [P, I64, I64, I, I, U64, U32, I, U16,
+                                              P, P, P, P, P, P, P]
         L.fp8_quantize_transpose.argtypes = [P, I64, I64, P, P, P, P]
+        L.swiglu_amax.argtypes = [P, I64, I64, I, U16, P, P, P, P]
+        L.swiglu_backward_amax.argtypes = [P, P, I64, I64, I, U16, P, P, P, P]
         L.bs_gemm.argtypes = [I, I64, I64, I64, P, P, P, P, P, P, P, I64, P]
-        for fn in ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "fp8_quantize_transpose",
-                   "bs_gemm"):
+        for fn in ABI_SYMBOLS[:-1]:
             getattr(L, fn).restype = I
         L.bsq_status_string.argtypes = [I]
         L.bsq_status_string.restype = ctypes.c_char_p
@@ -140,6 +144,66 @@ def quantize_transpose(x, fmt="nvfp4", block_rows=1, rnd="rne", seed=0, offset=0
         _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_amax"]), _stream(x.device))
     _check("quantize_transpose", st)
     return out
+
+
+def quantize_transpose_amax(x, amax_row, amax_col, block_rows=1, rnd="rne", seed=0, offset=0,
+                            rht_col=False, rht_signs=0, row=True, col=True):
+    """NVFP4 row and column outputs of x [R, C] under the given device amaxes
+    (f32 [1] each; the one of a skipped side may be None).
+
+    Returns a dict with row_codes, row_scales, col_codes, col_scales (None when skipped)."""
+    x = _check_input(x)
+    R, C = x.shape
+    out = dict(row_codes=None, row_scales=None, col_codes=None, col_scales=None)
+    if row:
+        out["row_codes"] = _u8((R, C // 2), x.device)
+        out["row_scales"] = _u8((R, C // 16), x.device)
+    if col:
+        out["col_codes"] = _u8((C, R // 2), x.device)
+        out["col_scales"] = _u8((C, R // 16), x.device)
+    st = lib().quantize_transpose_amax(
+        _ptr(x), R, C, int(block_rows), ROUNDING[rnd], int(seed), int(offset),
+        1 if rht_col else 0, int(rht_signs) & 0xFFFF, _ptr(amax_row), _ptr(amax_col),
+        _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["col_codes"]),
+        _ptr(out["col_scales"]), _stream(x.device))
+    _check("quantize_transpose_amax", st)
+    return out
+
+
+def swiglu(y_gu, rht_col=False, rht_signs=0, amax=True, out=None):
+    """H [T, F] = silu(G) * U of y_gu = [G | U] [T, 2F] (bf16), with amax_row =
+    max|H| and amax_col (the column RHT amax with rht_col, else max|H|).
+
+    Returns dict(h, amax_row, amax_col); the amaxes are None with amax=False."""
+    y = _check_input(y_gu)
+    T, F2 = y.shape
+    h = torch.empty((T, F2 // 2), dtype=torch.bfloat16, device=y.device) if out is None else out
+    ar = torch.empty(1, dtype=torch.float32, device=y.device) if amax else None
+    ac = torch.empty(1, dtype=torch.float32, device=y.device) if amax else None
+    st = lib().swiglu_amax(_ptr(y), T, F2 // 2, 1 if rht_col else 0, int(rht_signs) & 0xFFFF,
+                           _ptr(h), _ptr(ar), _ptr(ac), _stream(y.device))
+    _check("swiglu_amax", st)
+    return dict(h=h, amax_row=ar, amax_col=ac)
+
+
+def swiglu_backward(y_gu, d_h, rht_col=False, rht_signs=0, amax=True, out=None):
+    """dY_gu [T, 2F] = [dG | dU] from y_gu = [G | U] [T, 2F] and d_h [T, F]
+    (bf16), with the amaxes of dY_gu as for swiglu.
+
+    Returns dict(d_y_gu, amax_row, amax_col)."""
+    y = _check_input(y_gu)
+    d = _check_input(d_h)
+    T, F2 = y.shape
+    if d.shape != (T, F2 // 2):
+        raise ValueError("d_h must be [T, F] for y_gu [T, 2F]")
+    dy = torch.empty((T, F2), dtype=torch.bfloat16, device=y.device) if out is None else out
+    ar = torch.empty(1, dtype=torch.float32, device=y.device) if amax else None
+    ac = torch.empty(1, dtype=torch.float32, device=y.device) if amax else None
+    st = lib().swiglu_backward_amax(_ptr(y), _ptr(d), T, F2 // 2, 1 if rht_col else 0,
+                                    int(rht_signs) & 0xFFFF, _ptr(dy), _ptr(ar), _ptr(ac),
+                                    _stream(y.device))
+    _check("swiglu_backward_amax", st)
+    return dict(d_y_gu=dy, amax_row=ar, amax_col=ac)
 
 
 def fp8_quantize_transpose(x, row=True, col=True):

@@ -16,6 +16,34 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 bsq_status hip_status(hipError_t e) { return e == hipSuccess ? BSQ_OK : BSQ_EHIP; }
 
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+// Shared checks and dispatch of the SwiGLU forward (dh null) and backward.
+bsq_status swiglu_common(const void* y, const void* dh, int64_t rows, int64_t f, int rht_col,
+                         uint16_t signs, void* out, float* amax_row, float* amax_col, void* stream) {
+  if (rows < 0 || f < 0 || rows % 16 != 0 || f % 16 != 0) return BSQ_EINVAL;
+  if (!aligned4(amax_row) || !aligned4(amax_col)) return BSQ_EINVAL;
+  if (f >= ((int64_t)1 << 25)) return BSQ_EINVAL;    // 16 rows of y per buffer resource
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool amax = amax_row || amax_col;
+  if (rows * f == 0) return amax ? hip_status(bsq::launch_zero_amax(amax_row, amax_col, s)) : BSQ_OK;
+  const bool bwd = dh != nullptr;
+  if (!y || !out || !aligned16(y) || !aligned16(out) || !aligned16_or_null(dh)) return BSQ_EINVAL;
+  const int64_t ybytes = rows * f * 4, obytes = rows * f * (bwd ? 4 : 2);
+  if (overlap(out, obytes, y, ybytes) || (bwd && overlap(out, obytes, dh, rows * f * 2)))
+    return BSQ_EINVAL;
+  if (amax) {
+    const hipError_t e = bsq::launch_zero_amax(amax_row, amax_col, s);
+    if (e != hipSuccess) return BSQ_EHIP;
+  }
+  return hip_status(bsq::launch_swiglu(y, dh, rows, f, amax ? (rht_col ? 2 : 1) : 0, signs, out,
+                                       amax_row, amax_col, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,6 +184,44 @@ bsq_status fp8_quantize_transpose(const void* x, int64_t rows, int64_t cols, uin
   e = bsq::launch_amax_flat(x, rows * cols / 8, false, 0, amax, nullptr, s);
   if (e != hipSuccess) return BSQ_EHIP;
   return hip_status(bsq::launch_fp8_qt(x, rows, cols, amax, codes_row, codes_col, s));
+}
+
+bsq_status quantize_transpose_amax(const void* x, int64_t rows, int64_t cols, int block_rows,
+                                   bsq_rounding rnd, uint64_t seed, uint32_t offset, int rht_col,
+                                   uint16_t rht_signs, const float* amax_row, const float* amax_col,
+                                   uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,
+                                   uint8_t* scales_col, void* stream) {
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return BSQ_EINVAL;
+  if (block_rows != 1 && block_rows != 16) return BSQ_EINVAL;
+  if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
+  const bool do_row = codes_row || scales_row;
+  const bool do_col = codes_col || scales_col;
+  if (!do_row && !do_col) return BSQ_EINVAL;
+  if (block_rows == 16 && (rnd == BSQ_SR || rht_col)) return BSQ_EUNSUPPORTED;
+  if (rows * cols == 0) return BSQ_OK;
+  if (do_row && (!codes_row || !scales_row || !amax_row)) return BSQ_EINVAL;
+  if (do_col && (!codes_col || !scales_col || !amax_col)) return BSQ_EINVAL;
+  if (!aligned16_or_null(codes_row) || !aligned16_or_null(scales_row) ||
+      !aligned16_or_null(codes_col) || !aligned16_or_null(scales_col))
+    return BSQ_EINVAL;
+  if (!aligned4(amax_row) || !aligned4(amax_col)) return BSQ_EINVAL;
+  if (!x || !aligned16(x)) return BSQ_EINVAL;
+  return hip_status(bsq::launch_quant_tile(
+      bsq::kNVFP4, rnd == BSQ_SR, rht_col != 0 && do_col, block_rows == 16, x, rows, cols, do_row,
+      do_col, do_row ? amax_row : nullptr, do_col ? amax_col : nullptr, rht_signs, seed, offset,
+      codes_row, scales_row, codes_col, scales_col, static_cast<hipStream_t>(stream)));
+}
+
+bsq_status swiglu_amax(const void* y_gu, int64_t rows, int64_t f, int rht_col, uint16_t rht_signs,
+                       void* h, float* amax_row, float* amax_col, void* stream) {
+  return swiglu_common(y_gu, nullptr, rows, f, rht_col, rht_signs, h, amax_row, amax_col, stream);
+}
+
+bsq_status swiglu_backward_amax(const void* y_gu, const void* d_h, int64_t rows, int64_t f,
+                                int rht_col, uint16_t rht_signs, void* d_y_gu, float* amax_row,
+                                float* amax_col, void* stream) {
+  if (rows * f != 0 && !d_h) return BSQ_EINVAL;
+  return swiglu_common(y_gu, d_h, rows, f, rht_col, rht_signs, d_y_gu, amax_row, amax_col, stream);
 }
 
 bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,

@@ -21,6 +21,15 @@ __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xFFFF0000u); }
 
+// Two FP32 values -> a packed BF16 pair (lo in bits 0-15), rounded to nearest
+// even by the hardware pack: the same bits as the integer rounding rule for
+// every non-NaN input, denormals and ties included; NaN stays NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------- E2M1
 // Magnitude code (0..7) of a = |v| by round-to-nearest, ties to the even code,
 // saturating at 6 (OCP MX E2M1 element).

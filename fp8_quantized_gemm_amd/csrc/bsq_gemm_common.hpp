@@ -4,21 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bsq_device.hpp"   // pack_bf16x2
+
 namespace bsq {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
-
-// Two FP32 values -> a packed BF16 pair (lo in bits 0-15), rounded to nearest
-// even by the hardware pack: the same bits as the integer rounding rule for
-// every non-NaN input, denormals and ties included; NaN stays NaN.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // E4M3 byte SEL of w -> float (exact; OCP E4M3FN on gfx950).
 template <int SEL>

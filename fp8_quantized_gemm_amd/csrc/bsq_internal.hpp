@@ -27,6 +27,14 @@ hipError_t launch_amax_flat(const void* x, int64_t nchunk, bool rht, uint32_t si
 hipError_t launch_amax_tile_rht(const void* x, int64_t R, int64_t C, uint32_t signs,
                                 float* amax_row, float* amax_col, hipStream_t s);
 
+// SwiGLU of Y = [G | U] [R, 2F] (R % 16 == 0, F % 4 == 0): with dh null, the
+// forward H = silu(G) * U into out [R, F]; else the backward [dG | dU] of dh
+// [R, F] into out [R, 2F].  amax_mode 0: no amax; 1: max |out| into both amax
+// outputs (either may be null); 2: max |out| into amax_row and the column RHT
+// amax (16-row chunks) into amax_col.  Amax outputs must have been zeroed.
+hipError_t launch_swiglu(const void* y, const void* dh, int64_t R, int64_t F, int amax_mode,
+                         uint32_t signs, void* out, float* amax_row, float* amax_col, hipStream_t s);
+
 // Rowwise quantization over a contiguous tensor of nchunk 8-element chunks
 // (NVFP4 1x16 or MX 1x32 blocks; rows are implied since cols % block == 0).
 hipError_t launch_quant_flat(Fmt fmt, bool sr, bool rht, const void* x, int64_t nchunk,

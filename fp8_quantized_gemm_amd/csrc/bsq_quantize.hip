@@ -288,6 +288,160 @@ __global__ __launch_bounds__(256) void k_amax_tile_rht(const uint16_t* __restric
   block_max_atomic(f2u(mc * 0.25f), amax_col, nullptr);
 }
 
+// ---------------------------------------------------------------- SwiGLU producers
+// The MLP of the measured Llama models feeds the down projection with
+// H = silu(G) * U of the fused gate/up output Y = [G | U] [R, 2F], and its
+// backward turns dH into dY = [dG | dU].  Both are produced here together with
+// the per-tensor amaxes the NVFP4 quantizer of the output needs (plain, and the
+// column RHT amax when the column side is transformed), so the quantizer that
+// follows skips its own amax pass: one full read of the BF16 output less.
+//
+// A work item is 16 rows x 256 columns of H, one per wave; a lane owns 4
+// columns (8-byte loads, 512 contiguous bytes per wave and row), so the 16
+// values of a column chunk sit in one lane and the column RHT amax is
+// amax_rht_item on the rounded BF16 outputs: the standalone pass bit for bit.
+// Waves walk the items grid-stride (one atomic max per workgroup at the end).
+constexpr int kSwigluBlocks = 1024;                    // 4 workgroups per CU
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// sigma(g) and sigma(-g) = 1 - sigma(g), each without cancellation, from
+// e = exp(-|g|) (never overflows; the exp2 lowering keeps denormal results).
+// Relative error a few FP32 ulps (|g| log2(e) rounding, v_exp, v_rcp).
+struct SigPair { float s, c; };
+__device__ __forceinline__ SigPair sigmoid_pair(float g) {
+  const float e = exp2f(-fabsf(g) * kLog2e);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  const float er = e * r;
+  return g >= 0.0f ? SigPair{r, er} : SigPair{er, r};
+}
+
+__device__ __forceinline__ float swiglu1(float g, float u) { return g * sigmoid_pair(g).s * u; }
+
+// dG and dU of one element: dU = dH * silu(g), dG = dH * U * silu'(g) with
+// silu'(g) = sigma(g) * (1 + g * sigma(-g)).
+__device__ __forceinline__ void swiglu_bwd1(float g, float u, float d, float& dg, float& du) {
+  const SigPair p = sigmoid_pair(g);
+  du = d * (g * p.s);
+  dg = (d * u) * (p.s * (1.0f + g * p.c));
+}
+
+// Loads of one 16-row slab through a buffer resource (row i at scalar offset
+// i * row_bytes); dead lanes pass an offset beyond the resource and read zeros.
+__device__ __forceinline__ void slab_load(__amdgpu_buffer_rsrc_t rs, int voff, uint32_t row_bytes,
+                                          uint2 (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    v[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(i * row_bytes), 0));
+}
+
+__device__ __forceinline__ void slab_store(uint16_t* p, int64_t ld, const uint2 (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) *reinterpret_cast<uint2*>(p + i * ld) = v[i];
+}
+
+__device__ __forceinline__ void slab_max(const uint2 (&v)[16], ushort2v& mr) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    mr = __builtin_elementwise_max(mr, __builtin_bit_cast(ushort2v, v[i].x & 0x7FFF7FFFu));
+    mr = __builtin_elementwise_max(mr, __builtin_bit_cast(ushort2v, v[i].y & 0x7FFF7FFFu));
+  }
+}
+
+// AMAX: 0 none; 1 plain amax into both outputs; 2 plain amax into amax_row and
+// the column RHT amax into amax_col.
+template <int AMAX>
+__device__ __forceinline__ void swiglu_amax_out(ushort2v mr, float mc, float* amax_row, float* amax_col) {
+  if (AMAX == 0) return;
+  const uint32_t m = max((uint32_t)mr.x, (uint32_t)mr.y) << 16;
+  if (AMAX == 1) {
+    block_max_atomic(m, amax_row, amax_col);
+  } else {
+    block_max_atomic(m, amax_row, nullptr);
+    block_max_atomic(f2u(mc * 0.25f), amax_col, nullptr);
+  }
+}
+
+template <int AMAX>
+__global__ __launch_bounds__(256) void k_swiglu_fwd(const uint16_t* __restrict__ y, int64_t R,
+                                                    int64_t F, uint32_t signs, uint16_t* __restrict__ h,
+                                                    float* amax_row, float* amax_col) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ncg = (F + 255) / 256, nitems = ncg * (R / 16);
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const uint32_t yrow = (uint32_t)F * 4u;                 // bytes per row of Y
+  ushort2v mr = {0, 0};
+  float mc = 0.0f;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       it < nitems; it += nw) {
+    const int64_t rb = it / ncg, cg = it - rb * ncg;
+    const int64_t c0 = cg * 256 + lane * 4;
+    const bool live = c0 < F;
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(y + rb * 32 * F), (short)0, (int)(16u * yrow), kBufRsrcWord3);
+    uint2 g[16], u[16], hv[16];
+    slab_load(rs, live ? (int)(c0 * 2) : (int)0x7FFFFFF0, yrow, g);
+    slab_load(rs, live ? (int)((F + c0) * 2) : (int)0x7FFFFFF0, yrow, u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      hv[i].x = pack_bf16x2(swiglu1(bf16_lo(g[i].x), bf16_lo(u[i].x)), swiglu1(bf16_hi(g[i].x), bf16_hi(u[i].x)));
+      hv[i].y = pack_bf16x2(swiglu1(bf16_lo(g[i].y), bf16_lo(u[i].y)), swiglu1(bf16_hi(g[i].y), bf16_hi(u[i].y)));
+    }
+    if (live) slab_store(h + rb * 16 * F + c0, F, hv);
+    if (AMAX == 2) amax_rht_item(hv, signs, mr, mc);
+    else if (AMAX == 1) slab_max(hv, mr);
+  }
+  swiglu_amax_out<AMAX>(mr, mc, amax_row, amax_col);
+}
+
+template <int AMAX>
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const uint16_t* __restrict__ y,
+                                                    const uint16_t* __restrict__ dh, int64_t R,
+                                                    int64_t F, uint32_t signs, uint16_t* __restrict__ dy,
+                                                    float* amax_row, float* amax_col) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ncg = (F + 255) / 256, nitems = ncg * (R / 16);
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const uint32_t yrow = (uint32_t)F * 4u, drow = (uint32_t)F * 2u;
+  ushort2v mr = {0, 0};
+  float mc = 0.0f;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       it < nitems; it += nw) {
+    const int64_t rb = it / ncg, cg = it - rb * ncg;
+    const int64_t c0 = cg * 256 + lane * 4;
+    const bool live = c0 < F;
+    __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(y + rb * 32 * F), (short)0, (int)(16u * yrow), kBufRsrcWord3);
+    __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(dh + rb * 16 * F), (short)0, (int)(16u * drow), kBufRsrcWord3);
+    uint2 g[16], u[16], d[16], dg[16], du[16];
+    slab_load(ry, live ? (int)(c0 * 2) : (int)0x7FFFFFF0, yrow, g);
+    slab_load(ry, live ? (int)((F + c0) * 2) : (int)0x7FFFFFF0, yrow, u);
+    slab_load(rd, live ? (int)(c0 * 2) : (int)0x7FFFFFF0, drow, d);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float a0, a1, a2, a3, b0, b1, b2, b3;
+      swiglu_bwd1(bf16_lo(g[i].x), bf16_lo(u[i].x), bf16_lo(d[i].x), a0, b0);
+      swiglu_bwd1(bf16_hi(g[i].x), bf16_hi(u[i].x), bf16_hi(d[i].x), a1, b1);
+      swiglu_bwd1(bf16_lo(g[i].y), bf16_lo(u[i].y), bf16_lo(d[i].y), a2, b2);
+      swiglu_bwd1(bf16_hi(g[i].y), bf16_hi(u[i].y), bf16_hi(d[i].y), a3, b3);
+      dg[i] = make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+      du[i] = make_uint2(pack_bf16x2(b0, b1), pack_bf16x2(b2, b3));
+    }
+    if (live) {
+      slab_store(dy + rb * 32 * F + c0, 2 * F, dg);
+      slab_store(dy + rb * 32 * F + F + c0, 2 * F, du);
+    }
+    if (AMAX == 2) {
+      amax_rht_item(dg, signs, mr, mc);
+      amax_rht_item(du, signs, mr, mc);
+    } else if (AMAX == 1) {
+      slab_max(dg, mr);
+      slab_max(du, mr);
+    }
+  }
+  swiglu_amax_out<AMAX>(mr, mc, amax_row, amax_col);
+}
+
 // ---------------------------------------------------------------- rowwise encoder
 
 template <int FMT, bool SR, bool RHT>
@@ -846,6 +1000,31 @@ hipError_t launch_amax_tile_rht(const void* x, int64_t R, int64_t C, uint32_t si
   g = g < 1 ? 1 : (g > kAmaxRhtBlocks ? kAmaxRhtBlocks : g);
   hipLaunchKernelGGL(k_amax_tile_rht, dim3((unsigned)g), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), R, C, signs, amax_row, amax_col);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const void* y, const void* dh, int64_t R, int64_t F, int amax_mode,
+                         uint32_t signs, void* out, float* amax_row, float* amax_col, hipStream_t s) {
+  if (F * 64 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // 16 rows of Y per buffer resource
+  const int64_t nitems = ((F + 255) / 256) * (R / 16);
+  int64_t g = (nitems + 3) / 4;
+  g = g < 1 ? 1 : (g > kSwigluBlocks ? kSwigluBlocks : g);
+  const dim3 grid((unsigned)g), block(256);
+  const uint16_t* yp = static_cast<const uint16_t*>(y);
+  uint16_t* op = static_cast<uint16_t*>(out);
+#define BSQ_SWIGLU(A)                                                                              \
+  do {                                                                                             \
+    if (dh)                                                                                        \
+      hipLaunchKernelGGL(k_swiglu_bwd<A>, grid, block, 0, s, yp, static_cast<const uint16_t*>(dh), \
+                         R, F, signs, op, amax_row, amax_col);                                     \
+    else                                                                                           \
+      hipLaunchKernelGGL(k_swiglu_fwd<A>, grid, block, 0, s, yp, R, F, signs, op, amax_row,        \
+                         amax_col);                                                                \
+  } while (0)
+  if (amax_mode == 2) BSQ_SWIGLU(2);
+  else if (amax_mode == 1) BSQ_SWIGLU(1);
+  else BSQ_SWIGLU(0);
+#undef BSQ_SWIGLU
   return hipGetLastError();
 }
 

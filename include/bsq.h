@@ -154,6 +154,67 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
                               void* stream);
 
 /*
+ * NVFP4 row and column outputs of x[rows, cols] under per-tensor amaxes the
+ * caller already holds, typically from the producer of x (swiglu_amax,
+ * swiglu_backward_amax below): the encode pass of quantize_transpose without
+ * its amax pass.  Recipe ingredients 1-5 as for quantize_transpose with
+ * fmt = BSQ_NVFP4; given the amaxes quantize_transpose would compute, the
+ * codes and scales are the same bytes.
+ *   block_rows, rnd, seed, offset, rht_col, rht_signs : as quantize_transpose.
+ *   amax_row : in, device FP32 max|x|; required with the row outputs.
+ *   amax_col : in, device FP32 amax of the col side (max|RHT(x^T)| with
+ *              rht_col, else max|x|); required with the col outputs.
+ *   codes_row, scales_row / codes_col, scales_col : out, as quantize_transpose;
+ *              either pair may be NULL to skip that orientation (not both).
+ * Requires rows % 16 == 0 and cols % 16 == 0.
+ */
+bsq_status quantize_transpose_amax(const void* x, int64_t rows, int64_t cols, int block_rows,
+                                   bsq_rounding rnd, uint64_t seed, uint32_t offset, int rht_col,
+                                   uint16_t rht_signs, const float* amax_row, const float* amax_col,
+                                   uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,
+                                   uint8_t* scales_col, void* stream);
+
+/*
+ * SwiGLU forward of the MLP whose GEMMs the NVFP4 post measures (section
+ * "Performance results": Llama 3 8B and Llama 3.1 405B, whose MLP is the
+ * gate/up GEMM, SwiGLU, then the down GEMM), producing the BF16 input of the
+ * down projection together with the amaxes its NVFP4 quantizer needs (the
+ * data-flow paragraph after Figure 1: activations enter the next GEMM in
+ * NVFP4).  The pages give no SwiGLU formula; the reading used:
+ *   y_gu : in, BF16 [rows, 2f] = [G | U] (gate = first f columns).
+ *   h    : out, BF16 [rows, f], h = BF16_RNE(silu(G) * U), silu(g) =
+ *          g / (1 + exp(-g)); computed in FP32 (v_exp / v_rcp), so an element
+ *          may differ from the exactly rounded value by one BF16 ulp.
+ *   amax_row : out, device FP32 max|h| (or NULL).
+ *   amax_col : out, device FP32: with rht_col, max|RHT(h^T)| (16-row chunks,
+ *              rht_signs, the quantize_transpose rule); else max|h| (or NULL).
+ *              Both amaxes equal what quantize_transpose computes on h.
+ * With both amax pointers NULL only h is written.  h must not overlap y_gu.
+ * Requires rows % 16 == 0, f % 16 == 0 and f < 2^25.
+ */
+bsq_status swiglu_amax(const void* y_gu, int64_t rows, int64_t f, int rht_col, uint16_t rht_signs,
+                       void* h, float* amax_row, float* amax_col, void* stream);
+
+/*
+ * SwiGLU backward (the chain rule of h = silu(G) * U) producing the BF16
+ * gradient of the gate/up GEMM output with the amaxes of its NVFP4 quantizer
+ * (rowwise SR for DGRAD, columnwise SR + RHT for WGRAD: recipe ingredients 3
+ * and 5).
+ *   y_gu   : in, BF16 [rows, 2f] = [G | U], the forward's input.
+ *   d_h    : in, BF16 [rows, f], gradient of h.
+ *   d_y_gu : out, BF16 [rows, 2f] = [dG | dU], dU = BF16_RNE(dH * silu(G)),
+ *            dG = BF16_RNE(dH * U * silu'(G)), silu'(g) = sigma(g) *
+ *            (1 + g * (1 - sigma(g))); FP32 arithmetic, one BF16 ulp as for
+ *            swiglu_amax.
+ *   amax_row, amax_col : out, as for swiglu_amax, over d_y_gu.
+ * d_y_gu must not overlap y_gu or d_h.  Requires rows % 16 == 0, f % 16 == 0
+ * and f < 2^25.
+ */
+bsq_status swiglu_backward_amax(const void* y_gu, const void* d_h, int64_t rows, int64_t f,
+                                int rht_col, uint16_t rht_signs, void* d_y_gu, float* amax_row,
+                                float* amax_col, void* stream);
+
+/*
  * Per-tensor FP8 (E4M3) of x[rows, cols] (BF16) in both orientations from
  * one amax pass and one encode pass: the FP8 baseline's operands for FPROP
  * (rowwise), DGRAD (W columnwise) and WGRAD (dY and X columnwise).

@@ -117,6 +117,55 @@ def test_fp8_quantize_transpose_argument_errors():
     assert _qt(fmt=3) == bsq.BSQ_EUNSUPPORTED             # per-tensor FP8 has its own entry point
 
 
+def _qta(rows=32, cols=32, block_rows=1, rnd=0, rht=0, ar=FAKE, ac=FAKE, cr=FAKE, sr=FAKE,
+         cc=FAKE, sc=FAKE, x=FAKE):
+    return bsq.lib().quantize_transpose_amax(x, rows, cols, block_rows, rnd, 0, 0, rht, 0, ar, ac,
+                                             cr, sr, cc, sc, None)
+
+
+def test_quantize_transpose_amax_argument_errors():
+    assert _qta(rows=24) == bsq.BSQ_EINVAL                # rows % 16
+    assert _qta(cols=8) == bsq.BSQ_EINVAL                 # cols % 16
+    assert _qta(block_rows=2) == bsq.BSQ_EINVAL
+    assert _qta(rnd=5) == bsq.BSQ_EINVAL
+    assert _qta(cr=None, sr=None, cc=None, sc=None) == bsq.BSQ_EINVAL   # no output
+    assert _qta(ar=None) == bsq.BSQ_EINVAL                # row outputs need amax_row
+    assert _qta(ac=None) == bsq.BSQ_EINVAL                # col outputs need amax_col
+    assert _qta(sr=None) == bsq.BSQ_EINVAL                # half of the row pair
+    assert _qta(ac=FAKE + 2) == bsq.BSQ_EINVAL            # misaligned amax
+    assert _qta(cc=FAKE + 8) == bsq.BSQ_EINVAL            # misaligned codes
+    assert _qta(x=None) == bsq.BSQ_EINVAL
+    assert _qta(block_rows=16, rnd=1) == bsq.BSQ_EUNSUPPORTED
+    assert _qta(block_rows=16, rht=1) == bsq.BSQ_EUNSUPPORTED
+    assert _qta(rows=0) == bsq.BSQ_OK                     # empty: nothing to launch
+
+
+def _sw(rows=32, f=32, y=FAKE, h=FAKE + 0x100000, ar=None, ac=None, rht=0):
+    return bsq.lib().swiglu_amax(y, rows, f, rht, 0, h, ar, ac, None)
+
+
+def _swb(rows=32, f=32, y=FAKE, d=FAKE + 0x100000, out=FAKE + 0x200000, ar=None, ac=None):
+    return bsq.lib().swiglu_backward_amax(y, d, rows, f, 0, 0, out, ar, ac, None)
+
+
+def test_swiglu_argument_errors():
+    assert _sw(rows=24) == bsq.BSQ_EINVAL                 # rows % 16
+    assert _sw(f=40) == bsq.BSQ_EINVAL                    # f % 16
+    assert _sw(f=1 << 25) == bsq.BSQ_EINVAL               # 16 rows of y per buffer resource
+    assert _sw(y=None) == bsq.BSQ_EINVAL
+    assert _sw(h=None) == bsq.BSQ_EINVAL
+    assert _sw(h=FAKE + 8) == bsq.BSQ_EINVAL              # misaligned
+    assert _sw(h=FAKE + 32 * 32 * 2) == bsq.BSQ_EINVAL    # h overlaps the up half of y
+    assert _sw(ar=FAKE + 2) == bsq.BSQ_EINVAL             # misaligned amax
+    assert _sw(rows=0) == bsq.BSQ_OK and _sw(f=0) == bsq.BSQ_OK
+    assert _swb(d=None) == bsq.BSQ_EINVAL
+    assert _swb(d=FAKE + 8) == bsq.BSQ_EINVAL
+    assert _swb(out=FAKE + 0x100000 + 16) == bsq.BSQ_EINVAL   # out overlaps d_h
+    assert _swb(out=FAKE) == bsq.BSQ_EINVAL               # out overlaps y
+    assert _swb(rows=16, f=24) == bsq.BSQ_EINVAL
+    assert _swb(rows=0, d=None) == bsq.BSQ_OK
+
+
 def test_bs_gemm_argument_errors():
     L = bsq.lib()
     g = lambda fmt=0, M=16, N=16, K=32, ldc=16, a=FAKE, amax=FAKE, c=FAKE: L.bs_gemm(
