@@ -15,6 +15,13 @@ gate/up GEMM output.  The pages give no formula.  Readings:
   silu'(g) = sigma(g) * (1 + g * (1 - sigma(g))), sigma the logistic
   function; each output is evaluated in float64 and rounded once to BF16, and
   dY_gu = [dG | dU] [T, 2F] keeps the forward's column order.
+* Master-weight update: the data-flow paragraph after Figure 1 folds the
+  BF16 GEMM outputs into an FP32 master weight on the optimizer step and
+  names no optimizer.  The plainest fold is taken: w <- w - lr * dW, FP32
+  product then FP32 difference (two round-to-nearest-even steps, no fused
+  multiply-add), and the BF16 working copy the next step quantizes is
+  RNE(w).  Its amax (max |BF16 copy|) is the per-tensor amax the next step's
+  16x16 weight quantizer needs.
 """
 
 import numpy as np
@@ -64,3 +71,20 @@ def swiglu_backward(y_gu, d_h):
     g, u = y[:, :Fh], y[:, Fh:]
     return np.concatenate([f64_to_bf16_bits(dh * u * dsilu_f64(g)),
                            f64_to_bf16_bits(dh * silu_f64(g))], axis=1)
+
+
+def f64_to_f32(x):
+    """float64 -> nearest float32 (RNE), as float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def master_update(w32, grad_bf16, lr):
+    """FP32 master weight w32 (float32 array) and BF16 gradient bits ->
+    (new w32 float32, BF16 bits of the new weight, amax of that copy as float32)."""
+    w = np.asarray(w32, dtype=np.float32).astype(np.float64)
+    g = F.bf16_bits_to_f32(grad_bf16).astype(np.float64)
+    step = f64_to_f32(f64_to_f32(lr) * g)                  # FP32 product (exact in float64, then one rounding)
+    w_new = f64_to_f32(w - step)                           # FP32 difference, one rounding
+    bits = f64_to_bf16_bits(w_new)
+    amax = np.float32(np.abs(F.bf16_bits_to_f32(bits)).max(initial=0.0))
+    return w_new.astype(np.float32), bits, amax

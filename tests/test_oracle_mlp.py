@@ -9,6 +9,13 @@
   and with a central finite difference of silu; dY_gu agrees with autograd's
   vector-Jacobian product of silu(G) * U (rounded once to BF16), keeps the
   [dG | dU] order, and reduces to dG = dH * U / 2, dU = 0 at G = 0.
+* Master-weight update: lr = 0 and dW = 0 leave w unchanged; with lr a power
+  of two the product is exact and w - lr * dW rounds once (checked against
+  exact rational arithmetic); for a general lr the result lies within the
+  two-rounding bound ulp(lr * dW) / 2 + ulp(w') / 2 of the exact value, and
+  within ulp(lr * dW) + ulp(w') of torch.optim.SGD (no momentum), which
+  rounds once (fused multiply-add) on the CPU; the BF16 copy equals torch's
+  float32 -> bfloat16 cast and the amax is the largest magnitude.
 """
 
 import math
@@ -92,3 +99,52 @@ def test_swiglu_backward_at_zero_gate():
     d = M.swiglu_backward(y, dh)
     np.testing.assert_array_equal(F.bf16_bits_to_f32(d[:, :4]).astype(np.float64), [[1.5, -0.5, -0.5, 1.5]])
     assert not (d[:, 4:] & 0x7FFF).any()
+
+
+def _f32_ulp(x):
+    x = np.abs(np.asarray(x, dtype=np.float32))
+    return np.spacing(x).astype(np.float64)
+
+
+def test_master_update_identities_and_exact_cases():
+    from fractions import Fraction
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal(4096) * 0.02).astype(np.float32)
+    g = _bits(rng.standard_normal(4096) * 1e-2)
+    w0, b0, a0 = M.master_update(w, g, 0.0)
+    np.testing.assert_array_equal(w0, w)
+    wz, _, _ = M.master_update(w, np.zeros(4096, np.uint16), 0.5)
+    np.testing.assert_array_equal(wz, w)
+    # lr = 2^-7: lr * g is exact, so w - lr * g is rounded once
+    wn, _, _ = M.master_update(w[:256], g[:256], 2.0 ** -7)
+    gf = F.bf16_bits_to_f32(g[:256])
+    for i in range(256):
+        exact = Fraction(float(w[i])) - Fraction(2) ** -7 * Fraction(float(gf[i]))
+        assert wn[i] == np.float32(float(exact)) or abs(Fraction(float(wn[i])) - exact) <= Fraction(float(_f32_ulp(wn[i]))) / 2
+    # two roundings, not one: RN32(0.1f * 3) equals RN32(0.3), so the difference is exactly 0,
+    # where a fused multiply-add would leave 0.3f - 0.1f * 3 = 7.45e-9
+    w3, _, _ = M.master_update(np.array([0.3], np.float32), _bits([3.0]), np.float32(0.1))
+    assert w3[0] == 0.0
+    # BF16 copy and amax
+    want = torch.tensor(w0).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(b0, want)
+    assert a0 == np.float32(np.abs(torch.tensor(w0).to(torch.bfloat16).float().numpy()).max())
+
+
+def test_master_update_matches_sgd():
+    rng = np.random.default_rng(8)
+    n, lr = 50000, 3e-4
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = _bits(rng.standard_normal(n) * 10.0 ** rng.integers(-6, 1, n))
+    wn, bits, _ = M.master_update(w, g, lr)
+    p = torch.nn.Parameter(torch.tensor(w))
+    p.grad = torch.tensor(F.bf16_bits_to_f32(g))
+    torch.optim.SGD([p], lr=lr).step()
+    ref = p.detach().numpy().astype(np.float64)
+    prod = np.float64(np.float32(lr)) * F.bf16_bits_to_f32(g).astype(np.float64)   # exact in float64
+    exact = w.astype(np.float64) - prod
+    bound = _f32_ulp(prod) / 2 + _f32_ulp(wn) / 2
+    assert np.all(np.abs(wn.astype(np.float64) - exact) <= bound)
+    assert np.all(np.abs(wn.astype(np.float64) - ref) <= 2 * bound + _f32_ulp(ref))
+    # away from cancellation both routes round to the same value almost always
+    assert np.mean(wn.astype(np.float64) == ref) > 0.99
