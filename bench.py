@@ -19,7 +19,9 @@ FP8 baseline the NVFP4 post
 compares against (fp8_baseline: E4M3 under 448 / amax, FP8 matrix path, and
 the NVFP4 step's speed relative to it); the SwiGLU forward and backward
 around the H and dY_gu quantizers, with and without their fused amaxes
-(swiglu_fused_quantize); and the MX square workload (4096^3,
+(swiglu_fused_quantize); the whole chained MLP-layer training step with
+SwiGLU and the FP32 master-weight update (mlp_layer_step); and the MX square
+workload (4096^3,
 MXFP8 and MXFP4: mx_quantize of both operands + GEMM) on its own, with its
 roofline fraction.
 
@@ -316,6 +318,36 @@ def swiglu_fused(step, reps=10):
     return out
 
 
+def mlp_layer_step(step, steps, warmup, lr=1e-5):
+    """The whole MLP-layer training step chained through the C ABI
+    (fp8_quantized_gemm_amd.mlp.MLPLayer): quantizers, the six GEMMs, the
+    SwiGLU forward and backward with their fused amaxes, encode-only
+    quantizers of H and dY_gu and of the weights (amax from the update), and
+    the FP32 master-weight update of W_gu and W_down.  Same shapes and inputs
+    as the plain step (X, dY_down; W masters from the BF16 weights)."""
+    from fp8_quantized_gemm_amd.mlp import MLPLayer
+    t = step.t
+    layer = MLPLayer(t["W_gu"].float(), t["W_down"].float(), step.dims["tokens"], rht=bool(step.rht),
+                     rht_signs=step.signs, sr_seed=step.seed, lr=lr)
+    x, dy = t["X"], t["dY_down"]
+    for _ in range(max(1, warmup)):
+        layer.step(x, dy)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        layer.step(x, dy)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    out = {"ms_per_step": round(ms, 4), "value": round(layer.flops / (ms * 1e-3) / 1e12, 2),
+           "unit": "TFLOP/s (the six GEMMs' 2MNK over the whole layer step)",
+           "includes": "quantizers, 6 NVFP4 GEMMs, SwiGLU fwd/bwd with fused amaxes, "
+                       "FP32 master-weight update of W_gu and W_down"}
+    del layer
+    return out
+
+
 def mx_square(device, reps=20):
     """The MX workload (4096 x 4096 x 4096, A and B N(0,1) with outliers):
     rowwise mx_quantize of both operands, then the block-scaled GEMM, for MXFP8
@@ -521,6 +553,7 @@ def main():
         out["fp8_baseline"] = fp8_baseline(step, args.steps, args.warmup, ms)
     if not args.no_swiglu:
         out["swiglu_fused_quantize"] = swiglu_fused(step)
+        out["mlp_layer_step"] = mlp_layer_step(step, args.steps, args.warmup)
     if args.workload == "8b":
         out["rht_wgrad_error"] = rht_wgrad_error(step)
     if not args.no_mx:

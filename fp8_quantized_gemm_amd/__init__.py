@@ -20,8 +20,8 @@ BSQ_OK, BSQ_EINVAL, BSQ_EUNSUPPORTED, BSQ_EHIP = 0, 1, 2, 3
 FORMATS = {"nvfp4": 0, "mxfp4": 1, "mxfp8": 2, "fp8": 3}
 ROUNDING = {"rne": 0, "sr": 1}
 ABI_SYMBOLS = ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "quantize_transpose_amax",
-               "fp8_quantize_transpose", "swiglu_amax", "swiglu_backward_amax", "bs_gemm",
-               "bsq_status_string")
+               "fp8_quantize_transpose", "swiglu_amax", "swiglu_backward_amax",
+               "master_weight_update", "bs_gemm", "bsq_status_string")
 
 
 class BsqError(RuntimeError):
@@ -52,6 +52,7 @@ def lib():
         L.fp8_quantize_transpose.argtypes = [P, I64, I64, P, P, P, P]
         L.swiglu_amax.argtypes = [P, I64, I64, I, U16, P, P, P, P]
         L.swiglu_backward_amax.argtypes = [P, P, I64, I64, I, U16, P, P, P, P]
+        L.master_weight_update.argtypes = [P, P, I64, ctypes.c_float, P, P, P]
         L.bs_gemm.argtypes = [I, I64, I64, I64, P, P, P, P, P, P, P, I64, P]
         for fn in ABI_SYMBOLS[:-1]:
             getattr(L, fn).restype = I
@@ -204,6 +205,25 @@ def swiglu_backward(y_gu, d_h, rht_col=False, rht_signs=0, amax=True, out=None):
                                     _stream(y.device))
     _check("swiglu_backward_amax", st)
     return dict(d_y_gu=dy, amax_row=ar, amax_col=ac)
+
+
+def master_weight_update(w32, grad, lr, w_bf16=None, amax=True):
+    """In place w32 <- w32 - lr * grad (FP32 master weight, BF16 gradient of the
+    same shape); returns dict(w_bf16, amax) with the BF16 working copy and its
+    amax (None with amax=False)."""
+    if not (isinstance(w32, torch.Tensor) and w32.is_cuda and w32.dtype == torch.float32
+            and w32.is_contiguous()):
+        raise ValueError("w32 must be a contiguous float32 CUDA tensor (updated in place)")
+    if not (isinstance(grad, torch.Tensor) and grad.is_cuda and grad.dtype == torch.bfloat16
+            and grad.shape == w32.shape):
+        raise ValueError("grad must be a bfloat16 CUDA tensor shaped like w32")
+    g = grad.contiguous()
+    wb = torch.empty(w32.shape, dtype=torch.bfloat16, device=w32.device) if w_bf16 is None else w_bf16
+    a = torch.empty(1, dtype=torch.float32, device=w32.device) if amax else None
+    st = lib().master_weight_update(_ptr(w32), _ptr(g), w32.numel(), float(lr), _ptr(wb), _ptr(a),
+                                    _stream(w32.device))
+    _check("master_weight_update", st)
+    return dict(w_bf16=wb, amax=a)
 
 
 def fp8_quantize_transpose(x, row=True, col=True):

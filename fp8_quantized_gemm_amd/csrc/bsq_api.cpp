@@ -224,6 +224,23 @@ bsq_status swiglu_backward_amax(const void* y_gu, const void* d_h, int64_t rows,
   return swiglu_common(y_gu, d_h, rows, f, rht_col, rht_signs, d_y_gu, amax_row, amax_col, stream);
 }
 
+bsq_status master_weight_update(float* w32, const void* grad, int64_t n, float lr, void* w_bf16,
+                                float* amax, void* stream) {
+  if (n < 0 || n % 8 != 0 || !aligned4(amax)) return BSQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n == 0) return amax ? hip_status(bsq::launch_zero_amax(amax, nullptr, s)) : BSQ_OK;
+  if (!w32 || !grad || !w_bf16 || !aligned16(w32) || !aligned16(grad) || !aligned16(w_bf16))
+    return BSQ_EINVAL;
+  if (overlap(w32, n * 4, grad, n * 2) || overlap(w32, n * 4, w_bf16, n * 2) ||
+      overlap(grad, n * 2, w_bf16, n * 2))
+    return BSQ_EINVAL;
+  if (amax) {
+    const hipError_t e = bsq::launch_zero_amax(amax, nullptr, s);
+    if (e != hipSuccess) return BSQ_EHIP;
+  }
+  return hip_status(bsq::launch_master_update(w32, grad, n, lr, w_bf16, amax, s));
+}
+
 bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                    const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
                    const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,

@@ -35,6 +35,12 @@ hipError_t launch_amax_tile_rht(const void* x, int64_t R, int64_t C, uint32_t si
 hipError_t launch_swiglu(const void* y, const void* dh, int64_t R, int64_t F, int amax_mode,
                          uint32_t signs, void* out, float* amax_row, float* amax_col, hipStream_t s);
 
+// FP32 master-weight update of n elements (n % 8 == 0): w <- w - lr * g
+// (BF16 g), wb = BF16 RNE of the new w, and max |wb| into amax (zeroed
+// before; may be null).
+hipError_t launch_master_update(float* w, const void* g, int64_t n, float lr, void* wb, float* amax,
+                                hipStream_t s);
+
 // Rowwise quantization over a contiguous tensor of nchunk 8-element chunks
 // (NVFP4 1x16 or MX 1x32 blocks; rows are implied since cols % block == 0).
 hipError_t launch_quant_flat(Fmt fmt, bool sr, bool rht, const void* x, int64_t nchunk,

@@ -442,6 +442,49 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(const uint16_t* __restrict__
   swiglu_amax_out<AMAX>(mr, mc, amax_row, amax_col);
 }
 
+// ---------------------------------------------------------------- master-weight update
+// The optimizer step folds the BF16 weight gradient into the FP32 master
+// weight: w <- w - lr * dW as an FP32 product and an FP32 difference (this
+// file is built without multiply-add contraction), then writes the BF16
+// working copy RNE(w) that the next step quantizes, and reduces its amax (the
+// per-tensor amax of the next 16x16 weight quantization).  A lane moves one
+// 8-element chunk per trip: 16 bytes of gradient, 32 of w in and out, 16 of
+// the copy; grid-stride, one atomic max per workgroup.
+constexpr int kUpdateBlocks = 2048;
+
+template <bool AMAX>
+__global__ __launch_bounds__(256) void k_master_update(float* __restrict__ w, const uint4* __restrict__ g,
+                                                       int64_t nchunk, float lr, uint4* __restrict__ wb,
+                                                       float* amax) {
+  ushort2v m16 = {0, 0};
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride) {
+    const uint4 gv = g[c];
+    float4* wp = reinterpret_cast<float4*>(w) + 2 * c;
+    float4 a = wp[0], b = wp[1];
+    a.x = a.x - lr * bf16_lo(gv.x);
+    a.y = a.y - lr * bf16_hi(gv.x);
+    a.z = a.z - lr * bf16_lo(gv.y);
+    a.w = a.w - lr * bf16_hi(gv.y);
+    b.x = b.x - lr * bf16_lo(gv.z);
+    b.y = b.y - lr * bf16_hi(gv.z);
+    b.z = b.z - lr * bf16_lo(gv.w);
+    b.w = b.w - lr * bf16_hi(gv.w);
+    wp[0] = a;
+    wp[1] = b;
+    const uint4 o = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                               pack_bf16x2(b.z, b.w));
+    wb[c] = o;
+    if (AMAX) {
+      m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, o.x & 0x7FFF7FFFu));
+      m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, o.y & 0x7FFF7FFFu));
+      m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, o.z & 0x7FFF7FFFu));
+      m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2v, o.w & 0x7FFF7FFFu));
+    }
+  }
+  if (AMAX) block_max_atomic(max((uint32_t)m16.x, (uint32_t)m16.y) << 16, amax, nullptr);
+}
+
 // ---------------------------------------------------------------- rowwise encoder
 
 template <int FMT, bool SR, bool RHT>
@@ -1025,6 +1068,22 @@ hipError_t launch_swiglu(const void* y, const void* dh, int64_t R, int64_t F, in
   else if (amax_mode == 1) BSQ_SWIGLU(1);
   else BSQ_SWIGLU(0);
 #undef BSQ_SWIGLU
+  return hipGetLastError();
+}
+
+hipError_t launch_master_update(float* w, const void* g, int64_t n, float lr, void* wb, float* amax,
+                                hipStream_t s) {
+  const int64_t nchunk = n / 8;
+  int64_t grid = (nchunk + 255) / 256;
+  grid = grid < 1 ? 1 : (grid > kUpdateBlocks ? kUpdateBlocks : grid);
+  const uint4* gp = static_cast<const uint4*>(g);
+  uint4* wbp = static_cast<uint4*>(wb);
+  if (amax)
+    hipLaunchKernelGGL(k_master_update<true>, dim3((unsigned)grid), dim3(256), 0, s, w, gp, nchunk, lr,
+                       wbp, amax);
+  else
+    hipLaunchKernelGGL(k_master_update<false>, dim3((unsigned)grid), dim3(256), 0, s, w, gp, nchunk, lr,
+                       wbp, amax);
   return hipGetLastError();
 }
 

@@ -215,6 +215,23 @@ bsq_status swiglu_backward_amax(const void* y_gu, const void* d_h, int64_t rows,
                                 float* amax_col, void* stream);
 
 /*
+ * FP32 master-weight update of the optimizer step: the data-flow paragraph
+ * after Figure 1 of the NVFP4 post folds the BF16 GEMM outputs (here the
+ * WGRAD output dW) into an FP32 master weight; the pages name no optimizer,
+ * so the plain fold is used.  For each of the n elements:
+ *   w32[i]    <- FP32(w32[i] - FP32(lr * grad[i]))   (two RNE roundings, no FMA)
+ *   w_bf16[i] <- BF16_RNE(w32[i])                     (the copy the next step quantizes)
+ *   amax      <- max |w_bf16|                         (device FP32, or NULL)
+ * The amax is the per-tensor amax of the next 16x16 weight quantization
+ * (quantize_transpose_amax with block_rows 16, as amax_row and amax_col).
+ *   w32    : in/out, FP32 [n].       grad : in, BF16 [n].
+ *   w_bf16 : out, BF16 [n].  The three arrays must not overlap.
+ * Requires n % 8 == 0.
+ */
+bsq_status master_weight_update(float* w32, const void* grad, int64_t n, float lr, void* w_bf16,
+                                float* amax, void* stream);
+
+/*
  * Per-tensor FP8 (E4M3) of x[rows, cols] (BF16) in both orientations from
  * one amax pass and one encode pass: the FP8 baseline's operands for FPROP
  * (rowwise), DGRAD (W columnwise) and WGRAD (dY and X columnwise).

@@ -166,6 +166,19 @@ def test_swiglu_argument_errors():
     assert _swb(rows=0, d=None) == bsq.BSQ_OK
 
 
+def test_master_weight_update_argument_errors():
+    L = bsq.lib()
+    u = lambda n=64, w=FAKE, g=FAKE + 0x100000, wb=FAKE + 0x200000, a=None: L.master_weight_update(
+        w, g, n, 0.1, wb, a, None)
+    assert u(n=12) == bsq.BSQ_EINVAL                      # n % 8
+    assert u(n=-8) == bsq.BSQ_EINVAL
+    assert u(w=None) == bsq.BSQ_EINVAL and u(g=None) == bsq.BSQ_EINVAL and u(wb=None) == bsq.BSQ_EINVAL
+    assert u(g=FAKE + 8) == bsq.BSQ_EINVAL                # misaligned
+    assert u(wb=FAKE + 64) == bsq.BSQ_EINVAL              # copy overlaps w32
+    assert u(a=FAKE + 2) == bsq.BSQ_EINVAL                # misaligned amax
+    assert u(n=0) == bsq.BSQ_OK
+
+
 def test_bs_gemm_argument_errors():
     L = bsq.lib()
     g = lambda fmt=0, M=16, N=16, K=32, ldc=16, a=FAKE, amax=FAKE, c=FAKE: L.bs_gemm(
