@@ -12,21 +12,26 @@ One step = the whole hot path of one transformer-MLP layer on one GPU's share
           GEMM dW_gu = dY_gu^T . X
 value = sum(2 M N K) / step time, with BF16 inputs already resident in HBM.
 
-The same step is then timed with the RHT setting flipped (reported as rht_off
-or rht_on); the WGRAD_down error with and without the RHT is measured against
-an FP64 product (rht_wgrad_error, 8B only); the same step with the per-tensor
-FP8 baseline the NVFP4 post
-compares against (fp8_baseline: E4M3 under 448 / amax, FP8 matrix path, and
-the NVFP4 step's speed relative to it); the SwiGLU forward and backward
-around the H and dY_gu quantizers, with and without their fused amaxes
-(swiglu_fused_quantize); the whole chained MLP-layer training step with
-SwiGLU and the FP32 master-weight update (mlp_layer_step); and the MX square
-workload (4096^3,
-MXFP8 and MXFP4: mx_quantize of both operands + GEMM) on its own, with its
-roofline fraction.
+Also reported, each in its own field:
+  rht_off / rht_on       the same step with the RHT setting flipped;
+  rht_wgrad_error        WGRAD_down error with and without the RHT against an
+                         FP64 product (8B only);
+  fp8_baseline           the same step with the per-tensor FP8 baseline the
+                         NVFP4 post compares against (E4M3 under 448 / amax,
+                         FP8 matrix path) and the NVFP4 step's speed relative
+                         to it;
+  swiglu_fused_quantize  the SwiGLU forward and backward around the H and
+                         dY_gu quantizers, with and without their fused amaxes;
+  mlp_layer_step         the whole chained MLP-layer training step with SwiGLU
+                         and the FP32 master-weight update;
+  mx_square_4096         the MX square workload (4096^3, MXFP8 and MXFP4:
+                         mx_quantize of both operands + GEMM), with its
+                         roofline fraction;
+  nvfp4_route_ceilings   inner-loop ceilings of the two exact NVFP4 GEMM routes.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--no-rht]
-[--workload 8b|405b] [--no-cpu-baseline] [--no-mx] [--no-fp8] [--no-swiglu].
+[--workload 8b|405b] [--no-cpu-baseline] [--no-mx] [--no-fp8] [--no-swiglu]
+[--no-route-ceiling].
 """
 
 import argparse
@@ -348,6 +353,35 @@ def mlp_layer_step(step, steps, warmup, lr=1e-5):
     return out
 
 
+def route_ceilings(device, iters=4000, blocks=1024):
+    """Inner-loop ceilings of the two exact NVFP4 GEMM routes (operands in
+    registers, no memory): route (a), a per-16-K FP16 MFMA on unscaled E2M1
+    values plus the VALU rescale acc += sA * sB * P, against route (b)'s same
+    MFMAs accumulating directly.  Two timed launches each (HIP events on the
+    launch stream), the second reported."""
+    path = os.path.join(ROOT, "fp8_quantized_gemm_amd", "libbsq_ceiling.so")
+    L = ctypes.CDLL(path)
+    L.bsq_route_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.bsq_route_ceiling.restype = ctypes.c_int
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    sink = torch.zeros(blocks * 512, dtype=torch.float32, device=device)
+    flops = blocks * 8 * iters * 8 * 2.0 * 32 * 32 * 16
+    out = {}
+    for mode, key in ((1, "route_b_mfma_only"), (0, "route_a_mfma_plus_valu_rescale")):
+        for _ in range(2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            st = L.bsq_route_ceiling(mode, P(sink), iters, blocks, stream)
+            e1.record()
+            assert st == 0, st
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        out[key] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    out["note"] = ("FP16 MFMA loops with operands in registers; the complete route (b) GEMM "
+                   "(roofline.achieved) includes all memory traffic and the expansion")
+    return out
+
+
 def mx_square(device, reps=20):
     """The MX workload (4096 x 4096 x 4096, A and B N(0,1) with outliers):
     rowwise mx_quantize of both operands, then the block-scaled GEMM, for MXFP8
@@ -464,6 +498,8 @@ def main():
     ap.add_argument("--no-mx", action="store_true", help="skip the MX square-GEMM lines")
     ap.add_argument("--no-fp8", action="store_true", help="skip the per-tensor FP8 baseline step")
     ap.add_argument("--no-swiglu", action="store_true", help="skip the fused SwiGLU + quantize lines")
+    ap.add_argument("--no-route-ceiling", action="store_true",
+                    help="skip the inner-loop ceilings of the two NVFP4 GEMM routes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path "
@@ -558,6 +594,8 @@ def main():
         out["rht_wgrad_error"] = rht_wgrad_error(step)
     if not args.no_mx:
         out["mx_square_4096"] = mx_square(dev)
+    if not args.no_route_ceiling:
+        out["nvfp4_route_ceilings"] = route_ceilings(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, not args.no_rht)
     print(json.dumps(out))

@@ -2,7 +2,9 @@
 
 Usage: python -m fp8_quantized_gemm_amd._build   (or __graft_entry__.build()).
 Each translation unit is compiled to an object under _build/ in parallel,
-then linked into fp8_quantized_gemm_amd/libbsq.so.
+then linked into fp8_quantized_gemm_amd/libbsq.so.  The measurement kernels
+of the two GEMM routes' inner-loop ceilings go into a library of their own,
+libbsq_ceiling.so, so the product ABI stays what include/bsq.h declares.
 """
 
 import os
@@ -17,8 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsq.so")
+CEILING_LIB = os.path.join(PKG, "libbsq_ceiling.so")
 
 SOURCES = ["bsq_api.cpp", "bsq_quantize.hip", "bsq_gemm.hip", "bsq_gemm_nvfp4.hip"]
+CEILING_SOURCES = ["route_a_ceiling.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -50,22 +54,28 @@ def _compile(src):
     return obj, "\n".join(warn)
 
 
-def build(verbose=True):
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    objs = [o for o, _ in results]
-    for (o, w), s in zip(results, SOURCES):
-        if w and verbose:
-            print(f"[bsq build] {s}:\n{w}", file=sys.stderr)
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
+def build(verbose=True):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        results = list(ex.map(_compile, srcs))
+    for (o, w), s in zip(results, srcs):
+        if w and verbose:
+            print(f"[bsq build] {s}:\n{w}", file=sys.stderr)
+    objs = dict(zip(srcs, (o for o, _ in results)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CEILING_SOURCES], CEILING_LIB)
     if verbose:
-        print(f"[bsq build] wrote {LIB}", file=sys.stderr)
+        print(f"[bsq build] wrote {LIB} and {CEILING_LIB}", file=sys.stderr)
     return LIB
 
 
