@@ -20,6 +20,7 @@ sys.path.insert(0, ROOT)
 
 from fp8_quantized_gemm_amd import synth  # noqa: E402  (seeded input recipes only)
 from oracle import gemm as G  # noqa: E402
+from oracle import mlp as MLP  # noqa: E402
 from oracle import quantize as Q  # noqa: E402
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_cases.json")
@@ -100,6 +101,38 @@ def main():
     cases.append(dict(name="gemm_mxfp8", kind="gemm", fmt="mxfp8", M=32, N=16, K=512,
                       a_codes=hexa(ac), a_scales=hexa(as_), b_codes=hexa(bc), b_scales=hexa(bs),
                       c_ref=[repr(float(v)) for v in c_ref.ravel()]))
+
+    # per-tensor FP8 baseline, both orientations
+    x8 = bits((32, 48), 9114)
+    d8 = Q.fp8_quantize_transpose(x8)
+    cases.append(dict(name="fp8_qt", kind="fp8_quantize_transpose", shape=[32, 48], x=hexa(x8),
+                      out=dict(row_codes=hexa(d8["row_codes"]), col_codes=hexa(d8["col_codes"]),
+                               amax=f32hex(d8["amax"]))))
+
+    # SwiGLU forward and backward (F = 32) with the amaxes of their outputs
+    # (plain, and column RHT under the sign mask below)
+    signs = 0xB3C5
+    y = bits((16, 64), 9110, sigma=2.0)
+    h = MLP.swiglu(y)
+    qh = Q.quantize_transpose(h, "nvfp4", 1, "rne", rht_col=True, rht_signs=signs)
+    cases.append(dict(name="swiglu_fwd", kind="swiglu", shape=[16, 32], y=hexa(y), rht_signs=signs,
+                      out=dict(h=hexa(h), amax_row=f32hex(qh["row_amax"]),
+                               amax_col=f32hex(qh["col_amax"]))))
+    dh = bits((16, 32), 9111, sigma=1e-3, outliers=False)
+    dy = MLP.swiglu_backward(y, dh)
+    qd = Q.quantize_transpose(dy, "nvfp4", 1, "rne", rht_col=True, rht_signs=signs)
+    cases.append(dict(name="swiglu_bwd", kind="swiglu_backward", shape=[16, 32], y=hexa(y),
+                      dh=hexa(dh), rht_signs=signs,
+                      out=dict(dy=hexa(dy), amax_row=f32hex(qd["row_amax"]),
+                               amax_col=f32hex(qd["col_amax"]))))
+
+    # FP32 master-weight update with its BF16 copy and amax
+    w = (np.random.default_rng(9112).standard_normal(256) * 0.02).astype(np.float32)
+    g = bits((256,), 9113, sigma=1e-2, outliers=False)
+    lr = np.float32(1e-3)
+    wn, wb, wa = MLP.master_update(w, g, lr)
+    cases.append(dict(name="master_update", kind="master_update", n=256, lr=f32hex(lr), w=hexa(w),
+                      g=hexa(g), out=dict(w=hexa(wn), w_bf16=hexa(wb), amax=f32hex(wa))))
 
     with open(OUT, "w") as f:
         json.dump({"generator": "tests/golden/make_oracle_cases.py", "cases": cases}, f, indent=1)

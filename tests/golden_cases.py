@@ -36,3 +36,7 @@ def qt_shapes(R, C, fmt):
 
 def ids(cases):
     return [c["name"] for c in cases]
+
+
+def f32s(h):
+    return np.frombuffer(bytes.fromhex(h), dtype=np.float32).copy()

@@ -199,6 +199,18 @@ def test_bs_gemm_argument_errors():
     assert L.bs_gemm(1, 16, 16, 64, FAKE, None, None, FAKE, None, None, FAKE, 16, None) == bsq.BSQ_EINVAL
 
 
+def test_ceiling_library_loads_and_checks_arguments():
+    """The route-ceiling measurement kernels live in their own library."""
+    path = os.path.join(os.path.dirname(bsq.LIB_PATH), "libbsq_ceiling.so")
+    L = ctypes.CDLL(path)
+    L.bsq_route_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.bsq_route_ceiling.restype = ctypes.c_int
+    assert L.bsq_route_ceiling(2, FAKE, 1, 1, None) == -1        # no such mode
+    assert L.bsq_route_ceiling(0, None, 1, 1, None) == -1        # no sink
+    assert L.bsq_route_ceiling(1, FAKE, 1, 0, None) == -1        # no workgroups
+    assert not hasattr(bsq.lib(), "bsq_route_ceiling")           # not part of the product ABI
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(bsq, "_lib", None)
     monkeypatch.setattr(bsq, "LIB_PATH", "/nonexistent/libbsq.so")

@@ -41,15 +41,22 @@ def _key(b):
     return np.where(b & 0x8000, -mag, mag)
 
 
-def assert_within_one_ulp(got, want, what):
+def assert_within_one_ulp(got, want, what, max_off_fraction=MAX_OFF_FRACTION):
     got, want = np.asarray(got), np.asarray(want)
     assert got.shape == want.shape, (what, got.shape, want.shape)
     d = np.abs(_key(got) - _key(want))
     off = int((d != 0).sum())
     print(what, f"elements one ulp off: {off} of {d.size}")
     assert d.max(initial=0) <= 1, (what, int(d.max()), tuple(np.argwhere(d > 1)[0]))
-    assert off <= MAX_OFF_FRACTION * d.size, (what, off, d.size)
+    assert off <= max_off_fraction * d.size, (what, off, d.size)
     return off
+
+
+# Gates spread over [-120, 120]: the FP32 relative error grows like
+# (|g| + 5) 2^-24 (the rounding of |g| log2(e) before v_exp), about 65 2^-24
+# on average, and an element rounds to the other BF16 neighbour with
+# probability about twice that over the BF16 spacing 2^-8: ~0.2% expected.
+EXTREME_OFF_FRACTION = 5e-3
 
 
 def _amax_ref(h_bits, rht):
@@ -110,7 +117,7 @@ def test_swiglu_extreme_gates():
     d = bsq.swiglu(y, rht_col=True, rht_signs=SIGNS)
     torch.cuda.synchronize()
     h_ref = M.swiglu(bits(yb))
-    off = assert_within_one_ulp(bits(d["h"]), h_ref, "H extreme")
+    off = assert_within_one_ulp(bits(d["h"]), h_ref, "H extreme", EXTREME_OFF_FRACTION)
     _check_amaxes(d, d["h"], h_ref, True, off == 0, "H extreme")
 
 
@@ -139,7 +146,7 @@ def test_swiglu_backward_extreme_gates():
     d = bsq.swiglu_backward(yb.cuda(), dhb.cuda(), rht_col=True, rht_signs=SIGNS)
     torch.cuda.synchronize()
     ref = M.swiglu_backward(bits(yb), bits(dhb))
-    off = assert_within_one_ulp(bits(d["d_y_gu"]), ref, "dY_gu extreme")
+    off = assert_within_one_ulp(bits(d["d_y_gu"]), ref, "dY_gu extreme", EXTREME_OFF_FRACTION)
     _check_amaxes(d, d["d_y_gu"], ref, True, off == 0, "dY_gu extreme")
 
 
@@ -208,19 +215,19 @@ def _sample_rows(T, n, seed):
     return np.sort(np.random.default_rng(seed).choice(T, n, replace=False))
 
 
-def test_swiglu_8b_full_size_sampled():
-    """Llama 3 8B MLP shape (T = 32768 tokens, F = 14336): forward and backward
-    at full size in the launch configuration the benchmark times; 48 sampled
-    rows against the oracle, the amaxes against quantize_transpose on the
-    whole output."""
-    announce("swiglu 8b full size")
-    T, F = 32768, 14336
+@pytest.mark.parametrize("T,F", [(32768, 14336), (8192, 53248)], ids=["8b", "405b"])
+def test_swiglu_full_size_sampled(T, F):
+    """Llama 3 8B (T = 32768 tokens, F = 14336) and Llama 3.1 405B (T = 8192,
+    F = 53248) MLP shapes: forward and backward at full size in the launch
+    configuration the benchmark times; 48 sampled rows against the oracle,
+    the amaxes against quantize_transpose on the whole output."""
+    announce("swiglu full size", T, F)
     y = synth.bf16_tensor((T, 2 * F), 8701, 1.0, True, device="cuda")
     d = bsq.swiglu(y, rht_col=True, rht_signs=SIGNS)
     torch.cuda.synchronize()
     rows = _sample_rows(T, 48, 8702)
     yr = bits(y[torch.from_numpy(rows).cuda()])
-    assert_within_one_ulp(bits(d["h"][torch.from_numpy(rows).cuda()]), M.swiglu(yr), "H 8b sampled")
+    assert_within_one_ulp(bits(d["h"][torch.from_numpy(rows).cuda()]), M.swiglu(yr), "H sampled")
     q = bsq.quantize_transpose(d["h"], rht_col=True, rht_signs=SIGNS, row=True, col=True)
     torch.cuda.synchronize()
     assert f32(d["amax_row"])[0] == f32(q["row_amax"])[0]
@@ -230,7 +237,7 @@ def test_swiglu_8b_full_size_sampled():
     b = bsq.swiglu_backward(y, dh, rht_col=True, rht_signs=SIGNS)
     torch.cuda.synchronize()
     ridx = torch.from_numpy(rows).cuda()
-    assert_within_one_ulp(bits(b["d_y_gu"][ridx]), M.swiglu_backward(yr, bits(dh[ridx])), "dY_gu 8b sampled")
+    assert_within_one_ulp(bits(b["d_y_gu"][ridx]), M.swiglu_backward(yr, bits(dh[ridx])), "dY_gu sampled")
     q = bsq.quantize_transpose(b["d_y_gu"], rnd="sr", rht_col=True, rht_signs=SIGNS)
     torch.cuda.synchronize()
     assert f32(b["amax_row"])[0] == f32(q["row_amax"])[0]

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import gemm as G
+from oracle import mlp as MLP
 from oracle import quantize as Q
 
 import golden_cases as GC
@@ -35,6 +36,29 @@ def test_oracle_matches_stored_case(case):
         c, s = Q.mx_quantize(GC.u16(case["x"], (R, C)), fmt)
         np.testing.assert_array_equal(c, GC.u8(case["out"]["codes"], c.shape))
         np.testing.assert_array_equal(s, GC.u8(case["out"]["scales"], (R, C // 32)))
+    elif case["kind"] == "fp8_quantize_transpose":
+        R, C = case["shape"]
+        d = Q.fp8_quantize_transpose(GC.u16(case["x"], (R, C)))
+        np.testing.assert_array_equal(d["row_codes"], GC.u8(case["out"]["row_codes"], (R, C)))
+        np.testing.assert_array_equal(d["col_codes"], GC.u8(case["out"]["col_codes"], (C, R)))
+        assert np.float32(d["amax"]).tobytes() == np.float32(GC.f32(case["out"]["amax"])).tobytes()
+    elif case["kind"] in ("swiglu", "swiglu_backward"):
+        T, F = case["shape"]
+        y = GC.u16(case["y"], (T, 2 * F))
+        if case["kind"] == "swiglu":
+            out, key = MLP.swiglu(y), "h"
+        else:
+            out, key = MLP.swiglu_backward(y, GC.u16(case["dh"], (T, F))), "dy"
+        np.testing.assert_array_equal(out, GC.u16(case["out"][key], out.shape))
+        q = Q.quantize_transpose(out, "nvfp4", 1, "rne", rht_col=True, rht_signs=case["rht_signs"])
+        assert np.float32(q["row_amax"]) == GC.f32(case["out"]["amax_row"])
+        assert np.float32(q["col_amax"]) == GC.f32(case["out"]["amax_col"])
+    elif case["kind"] == "master_update":
+        wn, wb, wa = MLP.master_update(GC.f32s(case["w"]), GC.u16(case["g"], (case["n"],)),
+                                       GC.f32(case["lr"]))
+        np.testing.assert_array_equal(wn.view(np.uint32), GC.f32s(case["out"]["w"]).view(np.uint32))
+        np.testing.assert_array_equal(wb, GC.u16(case["out"]["w_bf16"], (case["n"],)))
+        assert wa == GC.f32(case["out"]["amax"])
     else:
         M, N, K, fmt = case["M"], case["N"], case["K"], case["fmt"]
         w = 1 if fmt == "mxfp8" else 2
