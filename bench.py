@@ -65,7 +65,7 @@ def P(t):
 class Step:
     """Preallocated buffers and the launch sequence of one MLP-layer step."""
 
-    def __init__(self, workload, rht, device):
+    def __init__(self, workload, rht, device, bx=True):
         self.dev = device
         self.lib = bsq.lib()
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
@@ -98,6 +98,13 @@ class Step:
             ("DGRAD_gu", ("dY_gu", "r"), ("W_gu", "c"), T, Hd, F2),
             ("WGRAD_gu", ("dY_gu", "c"), ("X", "c"), F2, Hd, T),
         ]
+        # GEMMs whose B operand is expanded to FP16 once (nvfp4_expand right
+        # after its quantization) and fed to bs_gemm_nvfp4_bx
+        self.bx = {g[0]: bx and bsq.bx_pays(g[4], g[5]) for g in self.gemms}
+        self.xb = {}
+        for g in self.gemms:
+            if self.bx[g[0]]:
+                self.xb[g[2]] = torch.empty((g[4], g[5]), dtype=torch.float16, device=device)
         self.flops = sum(2.0 * M * N * K for _, _, _, M, N, K in self.gemms)
         self.gemm_flops = {g[0]: 2.0 * g[3] * g[4] * g[5] for g in self.gemms}
         self.gemm_out = dict(FPROP_gu="Y_gu", FPROP_down="Y_down", DGRAD_down="dH",
@@ -117,12 +124,27 @@ class Step:
                                          P(b["cc"]), P(b["cs"]), P(b["ca"]), self.stream)
         assert st == 0, (name, bsq.status_string(st))
 
+    def expand(self, name):
+        """FP16 expansions of tensor `name`'s quantized orientations that a GEMM
+        takes pre-expanded."""
+        for (bn, bo), out in self.xb.items():
+            if bn != name:
+                continue
+            b = self.q[bn]
+            R, C = out.shape
+            st = self.lib.nvfp4_expand(P(b[bo + "c"]), P(b[bo + "s"]), R, C, P(out), self.stream)
+            assert st == 0, (name, bsq.status_string(st))
+
     def gemm(self, g):
         name, (an, ao), (bn, bo), M, N, K = g
         a, b = self.q[an], self.q[bn]
         c = self.out[self.gemm_out[name]]
-        st = self.lib.bs_gemm(NV, M, N, K, P(a[ao + "c"]), P(a[ao + "s"]), P(a[ao + "a"]),
-                              P(b[bo + "c"]), P(b[bo + "s"]), P(b[bo + "a"]), P(c), N, self.stream)
+        if self.bx[name]:
+            st = self.lib.bs_gemm_nvfp4_bx(M, N, K, P(a[ao + "c"]), P(a[ao + "s"]), P(a[ao + "a"]),
+                                           P(self.xb[(bn, bo)]), P(b[bo + "a"]), P(c), N, self.stream)
+        else:
+            st = self.lib.bs_gemm(NV, M, N, K, P(a[ao + "c"]), P(a[ao + "s"]), P(a[ao + "a"]),
+                                  P(b[bo + "c"]), P(b[bo + "s"]), P(b[bo + "a"]), P(c), N, self.stream)
         assert st == 0, (name, bsq.status_string(st))
 
     def run(self, events=None):
@@ -137,16 +159,22 @@ class Step:
             e.record()
             events.setdefault(name, []).append((s, e))
         G = {g[0]: g for g in self.gemms}
-        timed("q_X", lambda: self.quant("X", RNE, self.rht))
-        timed("q_W_gu", lambda: self.quant("W_gu", RNE, 0, 16))
+        expanded = {bn for bn, _ in self.xb}
+
+        def q(name, rnd, rht, block_rows=1):
+            timed("q_" + name, lambda: self.quant(name, rnd, rht, block_rows))
+            if name in expanded:
+                timed("x_" + name, lambda: self.expand(name))
+        q("X", RNE, self.rht)
+        q("W_gu", RNE, 0, 16)
         timed("FPROP_gu", lambda: self.gemm(G["FPROP_gu"]))
-        timed("q_H", lambda: self.quant("H", RNE, self.rht))
-        timed("q_W_down", lambda: self.quant("W_down", RNE, 0, 16))
+        q("H", RNE, self.rht)
+        q("W_down", RNE, 0, 16)
         timed("FPROP_down", lambda: self.gemm(G["FPROP_down"]))
-        timed("q_dY_down", lambda: self.quant("dY_down", SR, self.rht))
+        q("dY_down", SR, self.rht)
         timed("DGRAD_down", lambda: self.gemm(G["DGRAD_down"]))
         timed("WGRAD_down", lambda: self.gemm(G["WGRAD_down"]))
-        timed("q_dY_gu", lambda: self.quant("dY_gu", SR, self.rht))
+        q("dY_gu", SR, self.rht)
         timed("DGRAD_gu", lambda: self.gemm(G["DGRAD_gu"]))
         timed("WGRAD_gu", lambda: self.gemm(G["WGRAD_gu"]))
 
@@ -498,6 +526,8 @@ def main():
     ap.add_argument("--no-mx", action="store_true", help="skip the MX square-GEMM lines")
     ap.add_argument("--no-fp8", action="store_true", help="skip the per-tensor FP8 baseline step")
     ap.add_argument("--no-swiglu", action="store_true", help="skip the fused SwiGLU + quantize lines")
+    ap.add_argument("--no-bx", action="store_true",
+                    help="expand every B operand inside the GEMM (no pre-expanded weights)")
     ap.add_argument("--no-route-ceiling", action="store_true",
                     help="skip the inner-loop ceilings of the two NVFP4 GEMM routes")
     args = ap.parse_args()
@@ -508,7 +538,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    step = Step(args.workload, not args.no_rht, dev)
+    step = Step(args.workload, not args.no_rht, dev, bx=not args.no_bx)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step.run()
@@ -555,6 +585,10 @@ def main():
         k = "q_" + n
         breakdown[k] = {"ms": round(per[k], 4),
                         "gbs": round(step.quant_bytes[n] / (per[k] * 1e-3) / 1e9, 1)}
+        if "x_" + n in per:   # FP16 expansions: 0.5625 B read + 2 B written per element
+            nel = sum(o.numel() for (bn, _), o in step.xb.items() if bn == n)
+            breakdown["x_" + n] = {"ms": round(per["x_" + n], 4),
+                                   "gbs": round(2.5625 * nel / (per["x_" + n] * 1e-3) / 1e9, 1)}
     out = {
         "metric": "block-scaled GEMM TFLOP/s incl. quantize, Llama-3-8B MLP shapes; % MFMA peak",
         "value": round(value, 2),
@@ -574,7 +608,8 @@ def main():
                    "ffn": step.dims["ffn"], "rht": not args.no_rht,
                    "step_tflop": round(step.flops / 1e12, 3),
                    "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_nvfp4_pp (NVFP4 GEMM, 6 launches per step)",
+        "roofline": {"bound": "mfma", "kernel": ("NVFP4 GEMM, 6 launches per step: k_gemm_nvfp4_pp, and "
+                                                 "k_gemm_nvfp4_px for " + (", ".join(n for n, v in step.bx.items() if v) or "none")),
                      "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": gemm_traffic(args.workload),

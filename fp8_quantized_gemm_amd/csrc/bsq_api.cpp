@@ -241,6 +241,32 @@ bsq_status master_weight_update(float* w32, const void* grad, int64_t n, float l
   return hip_status(bsq::launch_master_update(w32, grad, n, lr, w_bf16, amax, s));
 }
 
+bsq_status nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                        void* out, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return BSQ_EINVAL;
+  if (rows * cols == 0) return BSQ_OK;
+  if (!codes || !scales || !out || !aligned16(out) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0)
+    return BSQ_EINVAL;
+  return hip_status(bsq::launch_nvfp4_expand(codes, scales, rows, cols, out,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+bsq_status bs_gemm_nvfp4_bx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                            const uint8_t* a_scales, const float* a_amax, const void* b_x,
+                            const float* b_amax, void* c, int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || ldc < N) return BSQ_EINVAL;
+  if (M > (int64_t)256 * 0x7FFFFF || N > (int64_t)256 * 0x7FFFFF) return BSQ_EINVAL;
+  if (M == 0 || N == 0) return BSQ_OK;
+  if (!a_codes || !a_scales || !b_x || !a_amax || !b_amax || !c) return BSQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(c) & 1u) != 0 || !aligned4(a_amax) || !aligned4(b_amax))
+    return BSQ_EINVAL;
+  if (K == 0 || K % 128 != 0 || !aligned16(a_codes) || !aligned4(a_scales) || !aligned16(b_x) ||
+      M * (K / 2) >= ((int64_t)1 << 32) || N * K * 2 >= ((int64_t)1 << 32))
+    return BSQ_EUNSUPPORTED;
+  return hip_status(bsq::launch_gemm_nvfp4_bx(M, N, K, a_codes, a_scales, a_amax, b_x, b_amax, c,
+                                              ldc, static_cast<hipStream_t>(stream)));
+}
+
 bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                    const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
                    const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,

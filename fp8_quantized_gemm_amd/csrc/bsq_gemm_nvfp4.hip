@@ -549,6 +549,194 @@ __global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_pp(
   nv_epilogue(acc, smem, a_amax, b_amax, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
 }
 
+// ---------------------------------------------------------------- pre-expanded B operand
+// The same ping-pong kernel with B handed over already expanded: an FP16
+// matrix Bx [N, K] holding v * S * 2^-7 for every element (the exact values
+// the in-kernel expansion produces, written once by k_nvfp4_expand).  Group 1
+// then expands nothing: in its memory slot it copies B half-stages from Bx
+// into a ring of LDS buffers with global -> LDS direct loads, D half-stages
+// ahead, and its MFMA slot holds the 16 MFMAs alone.  Group 0 is unchanged
+// (it stages and expands A), except that it reads B fragments from the ring.
+// Ring buffers hold 256 rows x 64 bytes (one half-stage); 16-byte chunk c of
+// row r sits in slot c ^ ((r >> 2) & 3), so both the direct loads (16 rows of
+// 64 contiguous bytes per instruction) and the fragment reads (one chunk of 16
+// consecutive rows per 16 lanes) avoid bank conflicts.
+constexpr int kPxRingB = 256 * 64;                       // one B half-stage
+constexpr int kPxD = 4;                                  // B half-stages issued ahead
+constexpr int kPxNB = kPxD + 1;                          // ring buffers
+constexpr int kPxABufB = kPpOpB;                         // one A half-stage (80-byte rows)
+constexpr int kPxStOff = 2 * kPxABufB;                   // A staging after the two A buffers
+constexpr int kPxRingOff = kPxStOff + 2 * kPpStB;        // B ring after the A staging
+constexpr int kPxLds = kPxRingOff + kPxNB * kPxRingB;    // 159744
+static_assert(kPxLds >= kEpiLds && kPxLds <= 160 * 1024, "pre-expanded-B LDS plan");
+
+// Direct loads of B half-stage `hs` (FP16, rows n0 .. n0 + 255 of Bx) into the
+// ring buffer at LDS address `dst`: wave w of group 1 copies rows 64 w .. 64 w
+// + 63, four instructions of 16 rows x 64 bytes.  Rows past N re-read the last
+// row (their results are never stored).  32-bit offsets: N * K * 2 < 2^32.
+__device__ __forceinline__ void px_stage_b(const uint8_t* bx, int64_t n0, int64_t N, int64_t K,
+                                           int64_t hs, uint32_t dst, int w, int lane) {
+  const uint8_t* src = bx + hs * 64;                     // K offset of the half-stage, in bytes
+  const uint32_t row_b = (uint32_t)K * 2u, last = (uint32_t)(N - 1), b32 = (uint32_t)n0;
+  const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t gr = min(b32 + (uint32_t)(w * 64 + q * 16 + (lane >> 2)), last);
+    dma_to_lds<16>(src, gr * row_b + chunk * 16, dst + (w * 64 + q * 16) * 64);
+  }
+}
+
+// Fragment reads of one half-stage: A from its 80-byte-row buffer, B from a
+// ring buffer.
+template <int S>
+__device__ __forceinline__ void px_frags(PpFrags& f, const uint8_t* abuf, const uint8_t* ring,
+                                         int wm, int wn, int h, int l32) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+    f.a[S][mi] = *reinterpret_cast<const halfx8*>(abuf + (wm * 128 + mi * 32 + l32) * kPpRowB + S * 32 + h * 16);
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int r = wn * 64 + ni * 32 + l32;
+    f.b[S][ni] = *reinterpret_cast<const halfx8*>(ring + r * 64 + (((2 * S + h) ^ ((r >> 2) & 3)) << 4));
+  }
+}
+
+__device__ __forceinline__ void px_pin_acc(floatx16 (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]));
+}
+
+// Group 1's MFMA slot: the 16 MFMAs of a half-stage and nothing else.
+__device__ __forceinline__ void px_mfma_only(floatx16 (&acc)[4][2], const PpFrags& f) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int st = k >> 3, mi = (k & 7) >> 1, ni = k & 1;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[st][ni], f.a[st][mi], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+// Group 0, half-stage j = 4 J + U (as pp_turn0, B fragments from the ring).
+template <int U>
+__device__ __forceinline__ void px_turn0(floatx16 (&acc)[4][2], PpFrags& f, PpRaw& raw,
+                                         uint8_t* smem, const PpSrc& s, int64_t J, int r,
+                                         int dst_off, int wm, int wn, int h, int l32, int lane) {
+  const int64_t j = 4 * J + U;
+  pp_mfma_slot<(U + 1) & 1>(acc, f, raw, smem + ((U + 1) & 1) * kPxABufB + dst_off);
+  pp_sync();
+  if (U == 2) pp_wait_staged<0>();
+  raw = pp_raw<(U + 2) & 3>(s.st + ((J + ((U + 2) >> 2)) & 1) * kPpStB, r);
+  const uint8_t* ring = smem + kPxRingOff + (int)((j + 1) % kPxNB) * kPxRingB;
+  px_frags<0>(f, smem + ((U + 1) & 1) * kPxABufB, ring, wm, wn, h, l32);
+  px_frags<1>(f, smem + ((U + 1) & 1) * kPxABufB, ring, wm, wn, h, l32);
+  if (U == 2) pp_stage_ahead(s, J, lane);
+  pp_sync();
+}
+
+// Group 1, half-stage j: slot 2j reads the fragments of j, issues B(j + D) and
+// waits for B(j + 1) (read by group 0 in slot 2j + 1); slot 2j + 1 runs the
+// MFMAs of j.  B(j + D) goes into the ring buffer of B(j - 1), which both
+// groups finished reading by slot 2j - 2.
+__device__ __forceinline__ void px_turn1(floatx16 (&acc)[4][2], PpFrags& f, uint8_t* smem,
+                                         uint32_t ring_lds, const uint8_t* bx, int64_t n0,
+                                         int64_t N, int64_t K, int64_t NH, int64_t j, int w,
+                                         int wm, int wn, int h, int l32, int lane) {
+  const uint8_t* ring = smem + kPxRingOff + (int)(j % kPxNB) * kPxRingB;
+  px_frags<0>(f, smem + (int)(j & 1) * kPxABufB, ring, wm, wn, h, l32);
+  px_frags<1>(f, smem + (int)(j & 1) * kPxABufB, ring, wm, wn, h, l32);
+  const int64_t hs = j + kPxD < NH ? j + kPxD : NH - 1;
+  px_stage_b(bx, n0, N, K, hs, ring_lds + (uint32_t)((j + kPxD) % kPxNB) * kPxRingB, w, lane);
+  pp_wait_staged<4 * (kPxD - 1)>();                     // B(j + 1) has landed
+  pp_sync();
+  px_mfma_only(acc, f);
+  px_pin_acc(acc);
+  pp_sync();
+}
+
+__global__ __launch_bounds__(kNvThreads) void k_gemm_nvfp4_px(
+    int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+    const float* __restrict__ a_amax, const uint8_t* bx, const float* __restrict__ b_amax,
+    uint16_t* __restrict__ c, int64_t ldc, int tiles_m, int tiles_n, int vec_store) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = wave >> 2;
+  const int wm = g, wn = wave & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int gs = __builtin_amdgcn_readfirstlane(g);
+  const int r = t & 255, w = __builtin_amdgcn_readfirstlane((t >> 6) & 3);
+  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const int64_t NH = K / 32;
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
+
+  PpFrags f;
+  if (gs == 0) {
+    PpSrc s;
+    s.codes = a_codes;
+    s.scales = a_scales;
+    s.base = m0;
+    s.rows = M;
+    s.code_ld = K / 2;
+    s.scale_ld = K / 16;
+    s.NQ = K / 128;
+    s.w = w;
+    s.st = smem + kPxStOff;
+    s.st_lds = smem_lds + kPxStOff;
+    const int dst_off = r * kPpRowB;
+    PpRaw raw;
+    pp_stage(s.codes, s.scales, s.base, s.rows, s.code_ld, s.scale_ld, 0, s.st_lds, w, lane);
+    pp_stage(s.codes, s.scales, s.base, s.rows, s.code_ld, s.scale_ld, s.NQ > 1 ? 1 : 0,
+             s.st_lds + kPpStB, w, lane);
+    pp_wait_staged<6>();                                          // quad 0 in
+    pp_expand<0>(pp_raw<0>(s.st, r), smem + dst_off);             // A(0)
+    pp_sync();                                                    // A(0) and B(0) visible
+    raw = pp_raw<1>(s.st, r);
+    px_frags<0>(f, smem, smem + kPxRingOff, wm, wn, h, l32);
+    px_frags<1>(f, smem, smem + kPxRingOff, wm, wn, h, l32);
+    for (int64_t J = 0; J < s.NQ; ++J) {
+      px_turn0<0>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      px_turn0<1>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      px_turn0<2>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+      px_turn0<3>(acc, f, raw, smem, s, J, r, dst_off, wm, wn, h, l32, lane);
+    }
+  } else {
+    const uint32_t ring_lds = smem_lds + kPxRingOff;
+#pragma unroll
+    for (int i = 0; i < kPxD; ++i)
+      px_stage_b(bx, n0, N, K, i < NH ? i : NH - 1, ring_lds + (uint32_t)i * kPxRingB, w, lane);
+    pp_wait_staged<4 * (kPxD - 1)>();                             // B(0) has landed
+    pp_sync();
+    for (int64_t j = 0; j < NH; ++j)
+      px_turn1(acc, f, smem, ring_lds, bx, n0, N, K, NH, j, w, wm, wn, h, l32, lane);
+  }
+  pp_wait_staged<0>();                                            // clamped tail loads landed
+  pp_sync();
+  nv_epilogue(acc, smem, a_amax, b_amax, c, ldc, M, N, m0, n0, wm, wn, lane, vec_store);
+}
+
+// FP16 expansion of an NVFP4 operand: out [R, K] = v * S * 2^-7 (exact), the
+// values the GEMM's in-kernel expansion produces.  A thread expands one
+// 16-element block per trip (8 code bytes, one scale byte, 32 output bytes).
+__global__ __launch_bounds__(256) void k_nvfp4_expand(const uint2* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      int64_t nblk, uint4* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+    const uint2 cw = codes[b];
+    const halfx2 s = nvfp4_scale_pair<0>((uint32_t)scales[b]);
+    out[2 * b] = __builtin_bit_cast(uint4, dequant8(cw.x, s));
+    out[2 * b + 1] = __builtin_bit_cast(uint4, dequant8(cw.y, s));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
@@ -579,6 +767,42 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
   else
     hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, block, kNvLds, s, M, N, K, ac, as, aa, bc, bs, ba,
                        cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace bsq
+
+namespace bsq {
+
+hipError_t launch_gemm_nvfp4_bx(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                                const float* aa, const void* bx, const float* ba, void* c,
+                                int64_t ldc, hipStream_t s) {
+  const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
+  const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+  if (!(K > 0 && K % 128 == 0 && al(ac, 16) && al(as, 4) && al(bx, 16) &&
+        M * (K / 2) < ((int64_t)1 << 32) && N * K * 2 < ((int64_t)1 << 32)))
+    return hipErrorNotSupported;
+  const bool vec_store = (ldc % 8 == 0) && al(c, 16);
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4_px),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPxLds) != hipSuccess)
+      return hipErrorInvalidConfiguration;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_gemm_nvfp4_px, dim3((unsigned)(tiles_m * tiles_n)), dim3(kNvThreads), kPxLds, s,
+                     M, N, K, ac, as, aa, static_cast<const uint8_t*>(bx), ba,
+                     static_cast<uint16_t*>(c), ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t K,
+                               void* out, hipStream_t s) {
+  const int64_t nblk = R * (K / 16);
+  int64_t g = (nblk + 255) / 256;
+  g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+  hipLaunchKernelGGL(k_nvfp4_expand, dim3((unsigned)g), dim3(256), 0, s,
+                     reinterpret_cast<const uint2*>(codes), scales, nblk, static_cast<uint4*>(out));
   return hipGetLastError();
 }
 

@@ -65,6 +65,16 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                              const float* aa, const uint8_t* bc, const uint8_t* bs,
                              const float* ba, void* c, int64_t ldc, hipStream_t s);
 
+// NVFP4 GEMM with B pre-expanded to FP16 (bx [N, K] = v * S * 2^-7, from
+// launch_nvfp4_expand).  hipErrorNotSupported unless K % 128 == 0, the
+// operands are 16-byte aligned (scales 4) and M * K / 2, N * K * 2 < 2^32.
+hipError_t launch_gemm_nvfp4_bx(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                                const float* aa, const void* bx, const float* ba, void* c,
+                                int64_t ldc, hipStream_t s);
+// FP16 expansion out [R, K] of NVFP4 codes [R, K/2] and scales [R, K/16].
+hipError_t launch_nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t K,
+                               void* out, hipStream_t s);
+
 // C[M, N] = alpha * A . B^T, block-scaled operands, BF16 out.
 hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,

@@ -7,7 +7,9 @@ SwiGLU MLP of the Llama models in "Performance results"):
 
   forward   q(X): rows RNE, columns RNE + RHT (amax pass + encode)
             q(W_gu), q(W_down): 16x16 tiles, under the amax the last update
-              of the master weight produced (encode only)
+              of the master weight produced (encode only); a weight orientation
+              whose FP16 copy stays cache-resident is expanded once
+              (nvfp4_expand) and its GEMMs take it pre-expanded
             Y_gu = X . W_gu^T;  H = SwiGLU(Y_gu), emitting H's amaxes
             q(H): rows RNE, columns RNE + RHT (encode only)
             Y_down = H . W_down^T
@@ -27,7 +29,7 @@ import ctypes
 
 import torch
 
-from . import lib as _lib, status_string
+from . import bx_pays, lib as _lib, status_string
 
 NV, RNE, SR = 0, 0, 1
 
@@ -72,6 +74,12 @@ class MLPLayer:
         self.act = dict(Y_gu=bf(T, F2), H=bf(T, F), Y_down=bf(T, Hd), dH=bf(T, F),
                         dY_gu=bf(T, F2), dX=bf(T, Hd))
         self.grad = {"W_gu": bf(F2, Hd), "W_down": bf(Hd, F)}
+        # B operands taken pre-expanded to FP16 (see bx_pays): (tensor, side) -> buffer
+        self.xb = {}
+        for name, b, side, N, K in (("FPROP_gu", "W_gu", "r", F2, Hd), ("FPROP_down", "W_down", "r", Hd, F),
+                                    ("DGRAD_down", "W_down", "c", F, Hd), ("DGRAD_gu", "W_gu", "c", Hd, F2)):
+            if bx_pays(N, K):
+                self.xb[(b, side)] = torch.empty((N, K), dtype=torch.float16, device=dev)
         self.flops = 2.0 * 3 * (T * F2 * Hd + T * Hd * F)
         # the BF16 working copies and their amaxes: an update with a zero gradient
         for k in self.w32:
@@ -98,8 +106,20 @@ class MLPLayer:
             _p(x), R, C, block_rows, rnd, self.seed, offset, rht, self.signs, _p(amax_row),
             _p(amax_col), _p(b["rc"]), _p(b["rs"]), _p(b["cc"]), _p(b["cs"]), self._stream()))
 
+    def _expand(self, name):
+        for (b, side), out in self.xb.items():
+            if b == name:
+                q, (R, C) = self.q[b], out.shape
+                self._ok("nvfp4_expand " + b, self.lib.nvfp4_expand(
+                    _p(q[side + "c"]), _p(q[side + "s"]), R, C, _p(out), self._stream()))
+
     def _gemm(self, what, a, ao, b, bo, c, M, N, K):
         qa, qb = self.q[a], self.q[b]
+        if (b, bo) in self.xb:
+            self._ok("bs_gemm_nvfp4_bx " + what, self.lib.bs_gemm_nvfp4_bx(
+                M, N, K, _p(qa[ao + "c"]), _p(qa[ao + "s"]), _p(qa[ao + "a"]), _p(self.xb[(b, bo)]),
+                _p(qb[bo + "a"]), _p(c), N, self._stream()))
+            return
         self._ok("bs_gemm " + what, self.lib.bs_gemm(
             NV, M, N, K, _p(qa[ao + "c"]), _p(qa[ao + "s"]), _p(qa[ao + "a"]), _p(qb[bo + "c"]),
             _p(qb[bo + "s"]), _p(qb[bo + "a"]), _p(c), N, self._stream()))
@@ -117,6 +137,7 @@ class MLPLayer:
         self._quant("X", x, RNE, self.rht, 0)
         wa = self.wamax["W_gu"]
         self._quant_amax("W_gu", self.wbf["W_gu"], 16, RNE, 0, 0, wa, wa)
+        self._expand("W_gu")
         self._gemm("FPROP_gu", "X", "r", "W_gu", "r", self.act["Y_gu"], T, 2 * F, Hd)
         H, qh = self.act["H"], self.q["H"]
         self._ok("swiglu_amax", self.lib.swiglu_amax(
@@ -125,6 +146,7 @@ class MLPLayer:
         self._quant_amax("H", H, 1, RNE, self.rht, 0, qh["ra"], qh["ca"])
         wa = self.wamax["W_down"]
         self._quant_amax("W_down", self.wbf["W_down"], 16, RNE, 0, 0, wa, wa)
+        self._expand("W_down")
         self._gemm("FPROP_down", "H", "r", "W_down", "r", self.act["Y_down"], T, Hd, F)
         return self.act["Y_down"]
 

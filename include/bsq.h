@@ -269,6 +269,38 @@ bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K,
                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_amax,
                    void* c, int64_t ldc, void* stream);
 
+/*
+ * FP16 expansion of an NVFP4 operand (recipe ingredients 1-2: E2M1 codes
+ * under E4M3 block scales), without its per-tensor scale:
+ *   out[r, k] = v * S * 2^-7   (FP16, exact: v * S has at most 6 significant
+ *                               bits and lies in [2^-10, 2688])
+ * with v the E2M1 value of element (r, k) and S its block's E4M3 scale.
+ *   codes  : in, uint8 [rows, cols/2] (8-byte aligned); scales : in, uint8 [rows, cols/16].
+ *   out    : out, FP16 [rows, cols].
+ * Requires cols % 16 == 0.  This is the B operand of bs_gemm_nvfp4_bx.
+ */
+bsq_status nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                        void* out, void* stream);
+
+/*
+ * The NVFP4 GEMM of bs_gemm (data-flow paragraph after Figure 1: FPROP,
+ * DGRAD, WGRAD consume NVFP4 operands, emit BF16) with B handed over as its
+ * FP16 expansion (nvfp4_expand of B's codes and scales): the kernel expands
+ * only A.  The result is bit-identical to bs_gemm(BSQ_NVFP4, ...) on the
+ * same operands.  For operands used by several GEMMs or much smaller than
+ * the other operand (weights, the smaller WGRAD input), expanding once and
+ * streaming FP16 costs less than expanding inside every output tile.
+ *   a_codes [M, K/2], a_scales [M, K/16], a_amax : the NVFP4 A operand.
+ *   b_x    : FP16 [N, K], nvfp4_expand of B;  b_amax : B's per-tensor amax.
+ *   c      : BF16 [M, N], row stride ldc; alpha = s_dec(a_amax) * s_dec(b_amax).
+ * BSQ_EUNSUPPORTED unless K % 128 == 0, K > 0, a_codes and b_x are 16-byte
+ * aligned, a_scales 4-byte aligned, M * K / 2 < 2^32 and N * K * 2 < 2^32
+ * (bs_gemm covers every other shape).
+ */
+bsq_status bs_gemm_nvfp4_bx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                            const uint8_t* a_scales, const float* a_amax, const void* b_x,
+                            const float* b_amax, void* c, int64_t ldc, void* stream);
+
 /* Static, human-readable name of a status code; host-side, thread-safe. */
 const char* bsq_status_string(bsq_status status);
 

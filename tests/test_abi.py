@@ -179,6 +179,22 @@ def test_master_weight_update_argument_errors():
     assert u(n=0) == bsq.BSQ_OK
 
 
+def test_expand_and_gemm_bx_argument_errors():
+    L = bsq.lib()
+    assert L.nvfp4_expand(FAKE, FAKE, 16, 24, FAKE, None) == bsq.BSQ_EINVAL       # cols % 16
+    assert L.nvfp4_expand(FAKE + 4, FAKE, 16, 32, FAKE, None) == bsq.BSQ_EINVAL   # codes 8-byte aligned
+    assert L.nvfp4_expand(FAKE, FAKE, 16, 32, FAKE + 8, None) == bsq.BSQ_EINVAL   # out 16-byte aligned
+    assert L.nvfp4_expand(None, FAKE, 16, 32, FAKE, None) == bsq.BSQ_EINVAL
+    assert L.nvfp4_expand(None, None, 0, 32, None, None) == bsq.BSQ_OK
+    g = lambda M=64, N=64, K=256, a=FAKE, bx=FAKE, amax=FAKE, c=FAKE, ldc=64: L.bs_gemm_nvfp4_bx(
+        M, N, K, a, FAKE, amax, bx, amax, c, ldc, None)
+    assert g(K=96) == bsq.BSQ_EUNSUPPORTED                 # K % 128
+    assert g(bx=FAKE + 8) == bsq.BSQ_EUNSUPPORTED          # B not 16-byte aligned
+    assert g(a=None) == bsq.BSQ_EINVAL and g(bx=None) == bsq.BSQ_EINVAL and g(amax=None) == bsq.BSQ_EINVAL
+    assert g(ldc=32) == bsq.BSQ_EINVAL
+    assert g(M=0) == bsq.BSQ_OK
+
+
 def test_bs_gemm_argument_errors():
     L = bsq.lib()
     g = lambda fmt=0, M=16, N=16, K=32, ldc=16, a=FAKE, amax=FAKE, c=FAKE: L.bs_gemm(
