@@ -581,7 +581,7 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   const bool fast = (K % C::BK == 0) && al16(ac) && al16(bc) && (code_ld % 16 == 0) &&
                     ((scale_ld * 1) % C::SB == 0) &&
                     ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(bs)) % C::SB == 0);
-  const bool vec_store = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(c) & 7) == 0);
+  const bool vec_store = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(c) & 7) == 0);   // 8-byte stores
   const size_t lds = 2 * (size_t)C::STAGE_BYTES;
   static bool attr_set = false;
   if (!attr_set) {
@@ -609,8 +609,10 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
         return hipErrorInvalidConfiguration;
       mx_attr_set = true;
     }
+    // its epilogue writes 16-byte row pieces: ldc % 8 == 0 and a 16-byte aligned c
+    const bool vec16 = (ldc % 8 == 0) && al16(c);
     hipLaunchKernelGGL((k_gemm_mx_pp<FMT>), grid, block, kMxLds, s, M, N, K, ac, as, aa, bc, bs, ba,
-                       cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
+                       cp, ldc, tiles_m, tiles_n, vec16 ? 1 : 0);
     return hipGetLastError();
   }
   if (fast)
