@@ -351,18 +351,26 @@ def swiglu_fused(step, reps=10):
     return out
 
 
-def mlp_layer_step(step, steps, warmup, lr=1e-5):
+def mlp_layer_step(step, steps, warmup, rel_update=1e-4):
     """The whole MLP-layer training step chained through the C ABI
     (fp8_quantized_gemm_amd.mlp.MLPLayer): quantizers, the six GEMMs, the
     SwiGLU forward and backward with their fused amaxes, encode-only
     quantizers of H and dY_gu and of the weights (amax from the update), and
     the FP32 master-weight update of W_gu and W_down.  Same shapes and inputs
-    as the plain step (X, dY_down; W masters from the BF16 weights)."""
+    as the plain step (X, dY_down; W masters from the BF16 weights).  The
+    learning rate is set from one untimed step so that an update moves each
+    master weight by about rel_update of its norm: the same inputs every step
+    with a fixed large rate would drive the weights, and then every operand,
+    to overflow within a few steps (the 405B gradients are N(0,1))."""
     from fp8_quantized_gemm_amd.mlp import MLPLayer
     t = step.t
     layer = MLPLayer(t["W_gu"].float(), t["W_down"].float(), step.dims["tokens"], rht=bool(step.rht),
-                     rht_signs=step.signs, sr_seed=step.seed, lr=lr)
+                     rht_signs=step.signs, sr_seed=step.seed, lr=0.0)
     x, dy = t["X"], t["dY_down"]
+    layer.step(x, dy)
+    torch.cuda.synchronize()
+    layer.lr = rel_update * min(float(layer.w32[k].norm() / layer.grad[k].float().norm())
+                                for k in ("W_gu", "W_down"))
     for _ in range(max(1, warmup)):
         layer.step(x, dy)
     torch.cuda.synchronize()
@@ -373,8 +381,11 @@ def mlp_layer_step(step, steps, warmup, lr=1e-5):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    finite = all(bool(torch.isfinite(v).all()) for v in (layer.act["Y_down"], layer.act["dX"],
+                                                          layer.w32["W_gu"], layer.w32["W_down"]))
     out = {"ms_per_step": round(ms, 4), "value": round(layer.flops / (ms * 1e-3) / 1e12, 2),
            "unit": "TFLOP/s (the six GEMMs' 2MNK over the whole layer step)",
+           "lr": layer.lr, "outputs_finite": finite,
            "includes": "quantizers, 6 NVFP4 GEMMs, SwiGLU fwd/bwd with fused amaxes, "
                        "FP32 master-weight update of W_gu and W_down"}
     del layer
