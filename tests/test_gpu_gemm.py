@@ -172,3 +172,31 @@ def test_nvfp4_tiny_scales_subnormal_products():
     ref = G.gemm_nvfp4(ac, as_, aa, bc, bs, ba)
     rep = _check(C, ref, "nvfp4 tiny scales")
     assert rep["frac_equal_rne"] > 0.99
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (1, 5, 48), (7, 1, 128), (3, 300, 16), (257, 1, 512)])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp8"])
+def test_degenerate_shapes(fmt, M, N, K):
+    """Single rows or columns and the smallest K of each format (one block)."""
+    if fmt != "nvfp4" and K % 32 != 0:
+        K = 32
+    announce("degenerate", fmt, M, N, K)
+    A = synth.bf16_tensor((M, K), 3000 + M + K, device="cuda")
+    B = synth.bf16_tensor((N, K), 4000 + N + K, sigma=0.02, outliers=False, device="cuda")
+    if fmt == "nvfp4":
+        ac, as_, aa = bsq.nvfp4_quantize(A, 1)
+        bc, bs, ba = bsq.nvfp4_quantize(B, 1)
+        C = bsq.bs_gemm(fmt, ac, as_, bc, bs, aa, ba)
+        oac, oas, oaa = Q.nvfp4_quantize(bits(A), 1)
+        obc, obs, oba = Q.nvfp4_quantize(bits(B), 1)
+        ref = G.gemm_nvfp4(oac, oas, oaa, obc, obs, oba)
+    else:
+        ac, as_ = bsq.mx_quantize(A, fmt)
+        bc, bs = bsq.mx_quantize(B, fmt)
+        C = bsq.bs_gemm(fmt, ac, as_, bc, bs, K=K)
+        oac, oas = Q.mx_quantize(bits(A), fmt)
+        obc, obs = Q.mx_quantize(bits(B), fmt)
+        ref = G.gemm_mx(oac, oas, obc, obs, fmt)
+    torch.cuda.synchronize()
+    assert C.shape == (M, N)
+    _check(C, ref, f"{fmt} {M}x{N}x{K}")
