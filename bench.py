@@ -492,7 +492,7 @@ def gemm_traffic(workload):
 
 
 def cpu_baseline(workload, rht):
-    """The oracle on a bounded slice of the same workload (10-25 s of host
+    """The oracle on a bounded slice of the same workload (about 10-25 s of host
     work): FPROP_gu for the first TOK tokens and the first NOUT output features (quantize X rows 1x16 RNE,
     W_gu rows 16x16 RNE, FP64 GEMM), with the per-tensor amax of both full
     tensors.  Reports TFLOP/s of that slice."""
@@ -504,7 +504,7 @@ def cpu_baseline(workload, rht):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         blas_threads = os.cpu_count() or 1
-    TOK, NOUT = 16384, 28672                  # 10-25 s with 16 host cores
+    TOK, NOUT = 24576, 28672                  # about 10-25 s with 16 host cores
     X = synth.workload_tensor(workload, "X", "cpu")
     W = synth.workload_tensor(workload, "W_gu", "cpu")
     bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
