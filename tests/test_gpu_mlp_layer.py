@@ -74,12 +74,13 @@ def test_master_update_twice_and_without_amax():
     assert_bytes_equal(bits(d2["w_bf16"]), b2, "copy twice")
 
 
-def test_master_update_8b_w_gu_full_size():
-    """W_gu of the 8B MLP (28672 x 4096 = 117.4M elements): every 4099th
-    element against the oracle; the amax against the whole BF16 copy."""
-    announce("master update 8b W_gu")
-    shape = (28672, 4096)
-    w = synth.bf16_tensor(shape, 9301, 0.02, False, device="cuda").float()
+@pytest.mark.parametrize("shape,sigma", [((28672, 4096), 0.02), ((106496, 16384), 0.01)], ids=["8b", "405b"])
+def test_master_update_w_gu_full_size(shape, sigma):
+    """W_gu of the 8B MLP (28672 x 4096 = 117.4M elements) and of the 405B MLP
+    (106496 x 16384 = 1.74G elements): every 4099th element against the
+    oracle; the amax against the whole BF16 copy."""
+    announce("master update W_gu", shape)
+    w = synth.bf16_tensor(shape, 9301, sigma, False, device="cuda").float()
     idx = torch.arange(0, w.numel(), 4099, device="cuda")
     w0 = w.view(-1)[idx].cpu().numpy()
     gr = synth.bf16_tensor(shape, 9302, 1e-3, False, device="cuda")
