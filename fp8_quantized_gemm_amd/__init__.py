@@ -82,6 +82,27 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_device(*tensors, out=None):
+    """Every given tensor (None skipped) is a contiguous CUDA tensor on one device,
+    and `out` a CUDA matrix with unit column stride (its row stride becomes ldc):
+    the library dereferences the raw pointers on the GPU."""
+    dev = None
+    for t in tensors + ((out,) if out is not None else ()):
+        if t is None:
+            continue
+        ok = isinstance(t, torch.Tensor) and t.is_cuda
+        if t is out:
+            ok = ok and t.dim() == 2 and (t.stride(1) == 1 or t.shape[1] <= 1)
+        else:
+            ok = ok and t.is_contiguous()
+        if not ok:
+            raise ValueError("operands must be contiguous CUDA tensors (out: rows with unit stride)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("operands must be on one device")
+
+
 def _check_input(x):
     if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2):
         raise ValueError("x must be a 2-D bfloat16 CUDA tensor")
@@ -96,6 +117,7 @@ def nvfp4_quantize(x, block_rows=1, rnd="rne", seed=0, offset=0, rht=False, rht_
                    amax=None):
     """Rowwise NVFP4 of x [R, C] -> (codes uint8 [R, C/2], scales uint8 [R, C/16], amax f32 [1])."""
     x = _check_input(x)
+    _check_device(x, amax)
     R, C = x.shape
     codes = _u8((R, C // 2), x.device)
     scales = _u8((R, max(C // 16, 0)), x.device)
@@ -157,6 +179,7 @@ def quantize_transpose_amax(x, amax_row, amax_col, block_rows=1, rnd="rne", seed
 
     Returns a dict with row_codes, row_scales, col_codes, col_scales (None when skipped)."""
     x = _check_input(x)
+    _check_device(x, amax_row, amax_col)
     R, C = x.shape
     out = dict(row_codes=None, row_scales=None, col_codes=None, col_scales=None)
     if row:
@@ -247,6 +270,7 @@ def fp8_quantize_transpose(x, row=True, col=True):
 def bs_gemm(fmt, a_codes, a_scales, b_codes, b_scales, a_amax=None, b_amax=None, K=None, out=None):
     """C [M, N] bf16 = alpha * deq(A) . deq(B)^T with A, B K-major block-scaled operands
     (per-tensor "fp8": scales None, amaxes required)."""
+    _check_device(a_codes, a_scales, b_codes, b_scales, a_amax, b_amax, out=out)
     M, N = a_codes.shape[0], b_codes.shape[0]
     if K is None:
         K = a_codes.shape[1] * (1 if fmt in ("mxfp8", "fp8") else 2)
@@ -274,6 +298,7 @@ def bx_pays(N, K):
 
 def nvfp4_expand(codes, scales, K=None, out=None):
     """FP16 [R, K] expansion v * S * 2^-7 of NVFP4 codes [R, K/2] + scales [R, K/16]."""
+    _check_device(codes, scales, out)
     R = codes.shape[0]
     if K is None:
         K = codes.shape[1] * 2
@@ -286,6 +311,7 @@ def nvfp4_expand(codes, scales, K=None, out=None):
 
 def bs_gemm_nvfp4_bx(a_codes, a_scales, a_amax, b_x, b_amax, out=None):
     """C [M, N] bf16 of NVFP4 A (codes, scales, amax) and FP16-expanded B [N, K]."""
+    _check_device(a_codes, a_scales, a_amax, b_x, b_amax, out=out)
     M, (N, K) = a_codes.shape[0], b_x.shape
     dev = a_codes.device
     if out is None:

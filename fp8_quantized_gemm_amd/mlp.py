@@ -45,6 +45,8 @@ class MLPLayer:
     copied).  tokens % 16 == 0, hidden % 16 == 0, F % 16 == 0."""
 
     def __init__(self, w_gu, w_down, tokens, rht=True, rht_signs=0, sr_seed=0, lr=1e-4):
+        if not (w_gu.is_cuda and w_down.is_cuda and w_gu.device == w_down.device):
+            raise ValueError("the master weights must be CUDA tensors on one device")
         dev = w_gu.device
         self.lib = _lib()
         self.dev = dev
@@ -133,7 +135,9 @@ class MLPLayer:
     # -- the step --------------------------------------------------------------------
     def forward(self, x):
         T, Hd, F = self.T, self.Hd, self.F
-        assert x.shape == (T, Hd) and x.dtype == torch.bfloat16 and x.is_contiguous()
+        if not (x.shape == (T, Hd) and x.dtype == torch.bfloat16 and x.is_contiguous()
+                and x.device == self.dev):
+            raise ValueError(f"x must be a contiguous bfloat16 [{T}, {Hd}] tensor on {self.dev}")
         self._quant("X", x, RNE, self.rht, 0)
         wa = self.wamax["W_gu"]
         self._quant_amax("W_gu", self.wbf["W_gu"], 16, RNE, 0, 0, wa, wa)
@@ -152,7 +156,9 @@ class MLPLayer:
 
     def backward(self, dy_down):
         T, Hd, F = self.T, self.Hd, self.F
-        assert dy_down.shape == (T, Hd) and dy_down.dtype == torch.bfloat16 and dy_down.is_contiguous()
+        if not (dy_down.shape == (T, Hd) and dy_down.dtype == torch.bfloat16 and dy_down.is_contiguous()
+                and dy_down.device == self.dev):
+            raise ValueError(f"dy_down must be a contiguous bfloat16 [{T}, {Hd}] tensor on {self.dev}")
         off = 2 * self.it
         self._quant("dY_down", dy_down, SR, self.rht, off)
         self._gemm("DGRAD_down", "dY_down", "r", "W_down", "c", self.act["dH"], T, F, Hd)

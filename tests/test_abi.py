@@ -232,3 +232,19 @@ def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(bsq, "LIB_PATH", "/nonexistent/libbsq.so")
     with pytest.raises(RuntimeError):
         bsq.lib()
+
+
+def test_binding_rejects_host_tensors():
+    """Host tensors never reach the library (it would dereference their
+    addresses on the GPU)."""
+    import torch
+    cpu = torch.zeros(16, 8, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        bsq.bs_gemm("nvfp4", cpu, cpu, cpu, cpu, K=16)
+    with pytest.raises(ValueError):
+        bsq.nvfp4_expand(cpu, cpu)
+    with pytest.raises(ValueError):
+        bsq.quantize_transpose(torch.zeros(16, 16, dtype=torch.bfloat16))
+    from fp8_quantized_gemm_amd.mlp import MLPLayer
+    with pytest.raises(ValueError):
+        MLPLayer(torch.zeros(32, 16), torch.zeros(16, 16), 16)
