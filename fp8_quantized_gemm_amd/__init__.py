@@ -205,6 +205,9 @@ def swiglu(y_gu, rht_col=False, rht_signs=0, amax=True, out=None):
     y = _check_input(y_gu)
     T, F2 = y.shape
     h = torch.empty((T, F2 // 2), dtype=torch.bfloat16, device=y.device) if out is None else out
+    _check_device(y, h)
+    if h.dtype != torch.bfloat16 or h.shape != (T, F2 // 2):
+        raise ValueError("out must be a bfloat16 [T, F] tensor")
     ar = torch.empty(1, dtype=torch.float32, device=y.device) if amax else None
     ac = torch.empty(1, dtype=torch.float32, device=y.device) if amax else None
     st = lib().swiglu_amax(_ptr(y), T, F2 // 2, 1 if rht_col else 0, int(rht_signs) & 0xFFFF,
@@ -224,6 +227,9 @@ def swiglu_backward(y_gu, d_h, rht_col=False, rht_signs=0, amax=True, out=None):
     if d.shape != (T, F2 // 2):
         raise ValueError("d_h must be [T, F] for y_gu [T, 2F]")
     dy = torch.empty((T, F2), dtype=torch.bfloat16, device=y.device) if out is None else out
+    _check_device(y, d, dy)
+    if dy.dtype != torch.bfloat16 or dy.shape != (T, F2):
+        raise ValueError("out must be a bfloat16 [T, 2F] tensor")
     ar = torch.empty(1, dtype=torch.float32, device=y.device) if amax else None
     ac = torch.empty(1, dtype=torch.float32, device=y.device) if amax else None
     st = lib().swiglu_backward_amax(_ptr(y), _ptr(d), T, F2 // 2, 1 if rht_col else 0,
@@ -245,6 +251,9 @@ def master_weight_update(w32, grad, lr, w_bf16=None, amax=True):
         raise ValueError("grad must be a bfloat16 CUDA tensor shaped like w32")
     g = grad.contiguous()
     wb = torch.empty(w32.shape, dtype=torch.bfloat16, device=w32.device) if w_bf16 is None else w_bf16
+    _check_device(w32, g, wb)
+    if wb.dtype != torch.bfloat16 or wb.numel() != w32.numel():
+        raise ValueError("w_bf16 must be a bfloat16 tensor with w32's element count")
     a = torch.empty(1, dtype=torch.float32, device=w32.device) if amax else None
     st = lib().master_weight_update(_ptr(w32), _ptr(g), w32.numel(), float(lr), _ptr(wb), _ptr(a),
                                     _stream(w32.device))
