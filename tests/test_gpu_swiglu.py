@@ -242,3 +242,40 @@ def test_swiglu_full_size_sampled(T, F):
     torch.cuda.synchronize()
     assert f32(b["amax_row"])[0] == f32(q["row_amax"])[0]
     assert f32(b["amax_col"])[0] == f32(q["col_amax"])[0]
+
+
+def _random_shapes(seed, n, max_rows=40, max_cols=70):
+    rng = np.random.default_rng(seed)
+    return [(16 * int(rng.integers(1, max_rows)), 16 * int(rng.integers(1, max_cols))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("R,F", _random_shapes(8801, 6))
+def test_swiglu_random_shapes(R, F):
+    """Seeded random multiples of 16 (the last 256-column group partly empty
+    in most of them): forward and backward with the column RHT amax."""
+    announce("swiglu random", R, F)
+    y = synth.bf16_tensor((R, 2 * F), 8900 + R + F, 1.5, True, device="cuda")
+    dh = synth.bf16_tensor((R, F), 8950 + R + F, 1e-2, False, device="cuda")
+    d = bsq.swiglu(y, rht_col=True, rht_signs=SIGNS)
+    b = bsq.swiglu_backward(y, dh, rht_col=True, rht_signs=SIGNS)
+    torch.cuda.synchronize()
+    h_ref = M.swiglu(bits(y))
+    off = assert_within_one_ulp(bits(d["h"]), h_ref, f"H {R}x{F}")
+    _check_amaxes(d, d["h"], h_ref, True, off == 0, f"H {R}x{F}")
+    g_ref = M.swiglu_backward(bits(y), bits(dh))
+    off = assert_within_one_ulp(bits(b["d_y_gu"]), g_ref, f"dY_gu {R}x{F}")
+    _check_amaxes(b, b["d_y_gu"], g_ref, True, off == 0, f"dY_gu {R}x{F}")
+
+
+@pytest.mark.parametrize("R,C", _random_shapes(8802, 6))
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+def test_quantize_transpose_amax_random_shapes(R, C, rnd):
+    announce("qt amax random", R, C, rnd)
+    x = synth.bf16_tensor((R, C), 9000 + R + C, 1.0, True, device="cuda")
+    ref = Q.quantize_transpose(bits(x), "nvfp4", 1, rnd, 0xABCDEF, 11, True, SIGNS)
+    ar = torch.tensor([ref["row_amax"]], dtype=torch.float32, device="cuda")
+    ac = torch.tensor([ref["col_amax"]], dtype=torch.float32, device="cuda")
+    d = bsq.quantize_transpose_amax(x, ar, ac, 1, rnd, 0xABCDEF, 11, True, SIGNS)
+    torch.cuda.synchronize()
+    for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+        assert_bytes_equal(u8(d[k]), ref[k], k)
