@@ -16,6 +16,10 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 bsq_status hip_status(hipError_t e) { return e == hipSuccess ? BSQ_OK : BSQ_EHIP; }
 
+// a * b would exceed 2^48 (no device holds that many elements; the bound also
+// keeps every byte offset the kernels form far inside int64).  a, b >= 0.
+bool too_many(int64_t a, int64_t b) { return a > 0 && b > (((int64_t)1 << 48) / a); }
+
 // [a, a + na) and [b, b + nb) share a byte.
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
@@ -26,6 +30,7 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 bsq_status swiglu_common(const void* y, const void* dh, int64_t rows, int64_t f, int rht_col,
                          uint16_t signs, void* out, float* amax_row, float* amax_col, void* stream) {
   if (rows < 0 || f < 0 || rows % 16 != 0 || f % 16 != 0) return BSQ_EINVAL;
+  if (too_many(rows, 2 * f)) return BSQ_EINVAL;
   if (!aligned4(amax_row) || !aligned4(amax_col)) return BSQ_EINVAL;
   if (f >= ((int64_t)1 << 25)) return BSQ_EINVAL;    // 16 rows of y per buffer resource
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -62,7 +67,7 @@ bsq_status nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int block_r
                           bsq_rounding rnd, uint64_t seed, uint32_t offset, int rht,
                           uint16_t rht_signs, const float* amax_in, uint8_t* codes,
                           uint8_t* scales, float* amax_out, void* stream) {
-  if (rows < 0 || cols < 0 || cols % 16 != 0) return BSQ_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || too_many(rows, cols)) return BSQ_EINVAL;
   if (block_rows != 1 && block_rows != 16) return BSQ_EINVAL;
   if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
   if (block_rows == 16 && rows % 16 != 0) return BSQ_EINVAL;
@@ -102,7 +107,7 @@ bsq_status nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int block_r
 bsq_status mx_quantize(const void* x, int64_t rows, int64_t cols, bsq_format fmt,
                        bsq_rounding rnd, uint64_t seed, uint32_t offset, uint8_t* codes,
                        uint8_t* scales, void* stream) {
-  if (rows < 0 || cols < 0 || cols % 32 != 0) return BSQ_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 32 != 0 || too_many(rows, cols)) return BSQ_EINVAL;
   if (fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8)
     return fmt == BSQ_NVFP4 || fmt == BSQ_FP8 ? BSQ_EUNSUPPORTED : BSQ_EINVAL;
   if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
@@ -127,6 +132,7 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
   const bool nv = fmt == BSQ_NVFP4;
   const int blk = nv ? 16 : 32;
   if (rows < 0 || cols < 0 || rows % blk != 0 || cols % blk != 0) return BSQ_EINVAL;
+  if (too_many(rows, cols)) return BSQ_EINVAL;
   if (block_rows != 1 && block_rows != 16) return BSQ_EINVAL;
   if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
   const bool do_row = codes_row || scales_row || (nv && amax_row);
@@ -173,6 +179,7 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
 bsq_status fp8_quantize_transpose(const void* x, int64_t rows, int64_t cols, uint8_t* codes_row,
                                   uint8_t* codes_col, float* amax, void* stream) {
   if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return BSQ_EINVAL;
+  if (too_many(rows, cols)) return BSQ_EINVAL;
   if (!amax || !aligned4(amax)) return BSQ_EINVAL;
   if (!codes_row && !codes_col) return BSQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -192,6 +199,7 @@ bsq_status quantize_transpose_amax(const void* x, int64_t rows, int64_t cols, in
                                    uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,
                                    uint8_t* scales_col, void* stream) {
   if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return BSQ_EINVAL;
+  if (too_many(rows, cols)) return BSQ_EINVAL;
   if (block_rows != 1 && block_rows != 16) return BSQ_EINVAL;
   if (rnd != BSQ_RNE && rnd != BSQ_SR) return BSQ_EINVAL;
   const bool do_row = codes_row || scales_row;
@@ -226,7 +234,7 @@ bsq_status swiglu_backward_amax(const void* y_gu, const void* d_h, int64_t rows,
 
 bsq_status master_weight_update(float* w32, const void* grad, int64_t n, float lr, void* w_bf16,
                                 float* amax, void* stream) {
-  if (n < 0 || n % 8 != 0 || !aligned4(amax)) return BSQ_EINVAL;
+  if (n < 0 || n % 8 != 0 || too_many(1, n) || !aligned4(amax)) return BSQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n == 0) return amax ? hip_status(bsq::launch_zero_amax(amax, nullptr, s)) : BSQ_OK;
   if (!w32 || !grad || !w_bf16 || !aligned16(w32) || !aligned16(grad) || !aligned16(w_bf16))
@@ -243,7 +251,7 @@ bsq_status master_weight_update(float* w32, const void* grad, int64_t n, float l
 
 bsq_status nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                         void* out, void* stream) {
-  if (rows < 0 || cols < 0 || cols % 16 != 0) return BSQ_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || too_many(rows, cols)) return BSQ_EINVAL;
   if (rows * cols == 0) return BSQ_OK;
   if (!codes || !scales || !out || !aligned16(out) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0)
     return BSQ_EINVAL;
@@ -255,6 +263,7 @@ bsq_status bs_gemm_nvfp4_bx(int64_t M, int64_t N, int64_t K, const uint8_t* a_co
                             const uint8_t* a_scales, const float* a_amax, const void* b_x,
                             const float* b_amax, void* c, int64_t ldc, void* stream) {
   if (M < 0 || N < 0 || K < 0 || ldc < N) return BSQ_EINVAL;
+  if (too_many(M, K) || too_many(N, K) || too_many(M, ldc)) return BSQ_EINVAL;
   if (M > (int64_t)256 * 0x7FFFFF || N > (int64_t)256 * 0x7FFFFF) return BSQ_EINVAL;
   if (M == 0 || N == 0) return BSQ_OK;
   if (!a_codes || !a_scales || !b_x || !a_amax || !b_amax || !c) return BSQ_EINVAL;
@@ -276,6 +285,7 @@ bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_
   if (M < 0 || N < 0 || K < 0) return BSQ_EINVAL;
   if (K % (fmt == BSQ_NVFP4 ? 16 : 32) != 0) return BSQ_EINVAL;
   if (ldc < N || ldc < 0) return BSQ_EINVAL;
+  if (too_many(M, K) || too_many(N, K) || too_many(M, ldc)) return BSQ_EINVAL;
   if (M > (int64_t)256 * 0x7FFFFF || N > (int64_t)256 * 0x7FFFFF) return BSQ_EINVAL;
   if (M == 0 || N == 0) return BSQ_OK;
   if (!c || ((reinterpret_cast<uintptr_t>(c) & 1u) != 0)) return BSQ_EINVAL;

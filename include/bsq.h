@@ -62,7 +62,9 @@
  *  - Inputs must be finite; NaN/Inf inputs give unspecified codes but never a
  *    fault.
  *  - Sizes: rows, cols, M, N, K >= 0; a zero-size call returns BSQ_OK and
- *    launches nothing except that amax outputs are set to 0.
+ *    launches nothing except that amax outputs are set to 0.  An element
+ *    count above 2^48 (rows * cols, n, M * K, N * K or M * ldc) returns
+ *    BSQ_EINVAL.
  */
 #ifndef BSQ_H
 #define BSQ_H

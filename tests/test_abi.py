@@ -248,3 +248,24 @@ def test_binding_rejects_host_tensors():
     from fp8_quantized_gemm_amd.mlp import MLPLayer
     with pytest.raises(ValueError):
         MLPLayer(torch.zeros(32, 16), torch.zeros(16, 16), 16)
+
+
+def test_element_counts_beyond_2_48_are_rejected():
+    """rows * cols (n, M * K, N * K, M * ldc) above 2^48 returns BSQ_EINVAL before
+    any size-dependent arithmetic can overflow."""
+    L, big = bsq.lib(), 1 << 40
+    assert _nv(rows=big, cols=1 << 16) == bsq.BSQ_EINVAL
+    assert _mx(rows=big, cols=1 << 16) == bsq.BSQ_EINVAL
+    assert _qt(rows=big, cols=1 << 16) == bsq.BSQ_EINVAL
+    assert _qt(fmt=1, rows=big, cols=1 << 16) == bsq.BSQ_EINVAL
+    assert _fp8(rows=big, cols=1 << 16) == bsq.BSQ_EINVAL
+    assert _qta(rows=big, cols=1 << 16) == bsq.BSQ_EINVAL
+    assert _sw(rows=big, f=1 << 10) == bsq.BSQ_EINVAL
+    assert L.master_weight_update(FAKE, FAKE + 0x100000, 1 << 49, ctypes.c_float(0.1),
+                                  FAKE + 0x200000, None, None) == bsq.BSQ_EINVAL
+    assert L.nvfp4_expand(FAKE, FAKE, big, 1 << 16, FAKE, None) == bsq.BSQ_EINVAL
+    for M, N, K, ldc in ((1 << 20, 16, 1 << 29, 16), (16, 1 << 20, 1 << 29, 1 << 20),
+                         (1 << 20, 16, 256, 1 << 29)):
+        assert L.bs_gemm(0, M, N, K, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ldc, None) == bsq.BSQ_EINVAL
+        assert L.bs_gemm(1, M, N, K, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, ldc, None) == bsq.BSQ_EINVAL
+        assert L.bs_gemm_nvfp4_bx(M, N, K, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ldc, None) == bsq.BSQ_EINVAL
