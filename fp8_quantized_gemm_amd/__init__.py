@@ -103,6 +103,37 @@ def _check_device(*tensors, out=None):
             raise ValueError("operands must be on one device")
 
 
+def _check_amax(*amaxes):
+    """Each given amax is a float32 tensor of at least one element."""
+    for a in amaxes:
+        if a is not None and not (isinstance(a, torch.Tensor) and a.dtype == torch.float32
+                                  and a.numel() >= 1):
+            raise ValueError("amax arguments must be float32 tensors of at least one element")
+
+
+def _check_operand(what, codes, scales, K, fmt):
+    """codes (uint8 [rows, K / elements-per-byte]) and scales (uint8 [rows, K /
+    block], None for per-tensor FP8) of one K-major GEMM operand.  The library
+    takes the row strides from K, so the widths must match exactly."""
+    per_byte = 1 if fmt in ("mxfp8", "fp8") else 2
+    blk = {"nvfp4": 16, "mxfp4": 32, "mxfp8": 32, "fp8": None}[fmt]
+    if not (isinstance(codes, torch.Tensor) and codes.dtype == torch.uint8 and codes.dim() == 2):
+        raise ValueError(f"{what} codes must be a 2-D uint8 tensor")
+    if K < 0 or K % per_byte or codes.shape[1] != K // per_byte:
+        raise ValueError(f"{what} codes are [{codes.shape[0]}, {codes.shape[1]}]; "
+                         f"K = {K} needs [rows, {K // per_byte}]")
+    if blk is None:
+        return
+    if not (isinstance(scales, torch.Tensor) and scales.dtype == torch.uint8 and scales.dim() == 2
+            and scales.shape[0] == codes.shape[0] and scales.shape[1] == K // blk):
+        raise ValueError(f"{what} scales must be uint8 [{codes.shape[0]}, {K // blk}]")
+
+
+def _check_out(out, M, N, dtype):
+    if out.dtype != dtype or tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be a {dtype} [{M}, {N}] tensor")
+
+
 def _check_input(x):
     if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2):
         raise ValueError("x must be a 2-D bfloat16 CUDA tensor")
@@ -118,6 +149,7 @@ def nvfp4_quantize(x, block_rows=1, rnd="rne", seed=0, offset=0, rht=False, rht_
     """Rowwise NVFP4 of x [R, C] -> (codes uint8 [R, C/2], scales uint8 [R, C/16], amax f32 [1])."""
     x = _check_input(x)
     _check_device(x, amax)
+    _check_amax(amax)
     R, C = x.shape
     codes = _u8((R, C // 2), x.device)
     scales = _u8((R, max(C // 16, 0)), x.device)
@@ -180,6 +212,7 @@ def quantize_transpose_amax(x, amax_row, amax_col, block_rows=1, rnd="rne", seed
     Returns a dict with row_codes, row_scales, col_codes, col_scales (None when skipped)."""
     x = _check_input(x)
     _check_device(x, amax_row, amax_col)
+    _check_amax(amax_row, amax_col)
     R, C = x.shape
     out = dict(row_codes=None, row_scales=None, col_codes=None, col_scales=None)
     if row:
@@ -279,10 +312,20 @@ def fp8_quantize_transpose(x, row=True, col=True):
 def bs_gemm(fmt, a_codes, a_scales, b_codes, b_scales, a_amax=None, b_amax=None, K=None, out=None):
     """C [M, N] bf16 = alpha * deq(A) . deq(B)^T with A, B K-major block-scaled operands
     (per-tensor "fp8": scales None, amaxes required)."""
-    _check_device(a_codes, a_scales, b_codes, b_scales, a_amax, b_amax, out=out)
-    M, N = a_codes.shape[0], b_codes.shape[0]
-    if K is None:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt!r}")
+    if K is None and isinstance(a_codes, torch.Tensor) and a_codes.dim() == 2:
         K = a_codes.shape[1] * (1 if fmt in ("mxfp8", "fp8") else 2)
+    K = int(K)
+    _check_operand("A", a_codes, a_scales, K, fmt)
+    _check_operand("B", b_codes, b_scales, K, fmt)
+    if fmt in ("nvfp4", "fp8") and (a_amax is None or b_amax is None):
+        raise ValueError(f"{fmt} needs both per-tensor amaxes")
+    _check_amax(a_amax, b_amax)
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    if out is not None:
+        _check_out(out, M, N, torch.bfloat16)
+    _check_device(a_codes, a_scales, b_codes, b_scales, a_amax, b_amax, out=out)
     dev = a_codes.device
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -307,10 +350,14 @@ def bx_pays(N, K):
 
 def nvfp4_expand(codes, scales, K=None, out=None):
     """FP16 [R, K] expansion v * S * 2^-7 of NVFP4 codes [R, K/2] + scales [R, K/16]."""
-    _check_device(codes, scales, out)
-    R = codes.shape[0]
-    if K is None:
+    if K is None and isinstance(codes, torch.Tensor) and codes.dim() == 2:
         K = codes.shape[1] * 2
+    K = int(K)
+    _check_operand("expand", codes, scales, K, "nvfp4")
+    R = codes.shape[0]
+    if out is not None:
+        _check_out(out, R, K, torch.float16)
+    _check_device(codes, scales, out)
     if out is None:
         out = torch.empty((R, K), dtype=torch.float16, device=codes.device)
     st = lib().nvfp4_expand(_ptr(codes), _ptr(scales), R, int(K), _ptr(out), _stream(codes.device))
@@ -320,8 +367,17 @@ def nvfp4_expand(codes, scales, K=None, out=None):
 
 def bs_gemm_nvfp4_bx(a_codes, a_scales, a_amax, b_x, b_amax, out=None):
     """C [M, N] bf16 of NVFP4 A (codes, scales, amax) and FP16-expanded B [N, K]."""
+    if not (isinstance(b_x, torch.Tensor) and b_x.dtype == torch.float16 and b_x.dim() == 2):
+        raise ValueError("b_x must be a 2-D float16 tensor (nvfp4_expand of B)")
+    N, K = b_x.shape
+    _check_operand("A", a_codes, a_scales, K, "nvfp4")
+    if a_amax is None or b_amax is None:
+        raise ValueError("nvfp4 needs both per-tensor amaxes")
+    _check_amax(a_amax, b_amax)
+    M = a_codes.shape[0]
+    if out is not None:
+        _check_out(out, M, N, torch.bfloat16)
     _check_device(a_codes, a_scales, a_amax, b_x, b_amax, out=out)
-    M, (N, K) = a_codes.shape[0], b_x.shape
     dev = a_codes.device
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)

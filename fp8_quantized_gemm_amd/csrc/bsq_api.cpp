@@ -4,7 +4,30 @@
 
 #include <hip/hip_runtime.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "bsq_internal.hpp"
+
+namespace bsq {
+
+hipError_t set_lds_limit(const void* fn, int bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, hipError_t> done;   // (device, kernel) -> result
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, fn);
+  const auto it = done.find(key);
+  if (it != done.end()) return it->second;
+  const hipError_t r = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  done.emplace(key, r);
+  return r;
+}
+
+}  // namespace bsq
 
 namespace {
 
@@ -206,6 +229,10 @@ bsq_status quantize_transpose_amax(const void* x, int64_t rows, int64_t cols, in
   const bool do_col = codes_col || scales_col;
   if (!do_row && !do_col) return BSQ_EINVAL;
   if (block_rows == 16 && (rnd == BSQ_SR || rht_col)) return BSQ_EUNSUPPORTED;
+  // 16x16 tiles encode both orientations under one amax (the codes of x^T
+  // are the codes of x transposed), so the caller must pass that one amax
+  // for both sides
+  if (block_rows == 16 && do_row && do_col && amax_row != amax_col) return BSQ_EINVAL;
   if (rows * cols == 0) return BSQ_OK;
   if (do_row && (!codes_row || !scales_row || !amax_row)) return BSQ_EINVAL;
   if (do_col && (!codes_col || !scales_col || !amax_col)) return BSQ_EINVAL;

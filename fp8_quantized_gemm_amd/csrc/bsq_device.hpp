@@ -90,10 +90,12 @@ __device__ __forceinline__ float div6(float a) {
 // saturating at 448.  The hardware FP32 -> E4M3 convert rounds to nearest
 // even and agrees with e4m3_rne_mag on [0, 464) (checked exhaustively); the
 // clamp maps everything above 448 (reachable only with a caller-supplied
-// amax below the true one) to 448, as e4m3_rne_mag does.
+// amax below the true one) to 448, as e4m3_rne_mag does.  sf is never
+// negative, so the code fits 7 bits; the mask keeps it below 128 even for
+// non-finite inputs, where it indexes the 128-entry encode-factor tables.
 __device__ __forceinline__ uint32_t nvfp4_scale_code(float a_b, float s_enc) {
   const float sf = fminf(div6(a_b) * s_enc, 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sf, 0.0f, 0, false) & 0xFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sf, 0.0f, 0, false) & 0x7Fu;
 }
 
 // Encode factor for every E4M3 scale code: enc = s_enc / S (0 for S == 0),

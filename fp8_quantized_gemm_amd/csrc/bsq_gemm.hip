@@ -583,15 +583,9 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
                     ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(bs)) % C::SB == 0);
   const bool vec_store = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(c) & 7) == 0);   // 8-byte stores
   const size_t lds = 2 * (size_t)C::STAGE_BYTES;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<FMT, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<FMT, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipErrorInvalidConfiguration;
-    attr_set = true;
-  }
+  if (set_lds_limit(reinterpret_cast<const void*>(&k_gemm<FMT, true>), (int)lds) != hipSuccess ||
+      set_lds_limit(reinterpret_cast<const void*>(&k_gemm<FMT, false>), (int)lds) != hipSuccess)
+    return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
   uint16_t* cp = static_cast<uint16_t*>(c);
   // staged kernel: whole 64-byte code segments per stage, 16-byte scale pieces
@@ -601,14 +595,9 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   const bool staged = K > 0 && (FMT == kFP8 ? K % 64 == 0 : K % 512 == 0) && al16(ac) && al16(bc) &&
                       (FMT == kFP8 || (al16(as) && al16(bs))) &&
                       M * code_ld < ((int64_t)1 << 32) && N * code_ld < ((int64_t)1 << 32);
-  static bool mx_attr_set = false;
   if (staged) {
-    if (!mx_attr_set) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx_pp<FMT>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds) != hipSuccess)
-        return hipErrorInvalidConfiguration;
-      mx_attr_set = true;
-    }
+    if (set_lds_limit(reinterpret_cast<const void*>(&k_gemm_mx_pp<FMT>), kMxLds) != hipSuccess)
+      return hipErrorInvalidConfiguration;
     // its epilogue writes 16-byte row pieces: ldc % 8 == 0 and a 16-byte aligned c
     const bool vec16 = (ldc % 8 == 0) && al16(c);
     hipLaunchKernelGGL((k_gemm_mx_pp<FMT>), grid, block, kMxLds, s, M, N, K, ac, as, aa, bc, bs, ba,

@@ -757,15 +757,9 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
   const bool fast = K > 0 && (K % 128 == 0) && al(ac, 16) && al(bc, 16) && al(as, 4) && al(bs, 4) &&
                     M * (K / 2) < ((int64_t)1 << 32) && N * (K / 2) < ((int64_t)1 << 32);
   const bool vec_store = (ldc % 8 == 0) && al(c, 16);
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4_pp),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPpLds) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kNvLds) != hipSuccess)
-      return hipErrorInvalidConfiguration;
-    attr_set = true;
-  }
+  if (set_lds_limit(reinterpret_cast<const void*>(&k_gemm_nvfp4_pp), kPpLds) != hipSuccess ||
+      set_lds_limit(reinterpret_cast<const void*>(&k_gemm_nvfp4<false>), kNvLds) != hipSuccess)
+    return hipErrorInvalidConfiguration;
   uint16_t* cp = static_cast<uint16_t*>(c);
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kNvThreads);
   if (fast)
@@ -790,13 +784,8 @@ hipError_t launch_gemm_nvfp4_bx(int64_t M, int64_t N, int64_t K, const uint8_t* 
         M * (K / 2) < ((int64_t)1 << 32) && N * K * 2 < ((int64_t)1 << 32)))
     return hipErrorNotSupported;
   const bool vec_store = (ldc % 8 == 0) && al(c, 16);
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_nvfp4_px),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPxLds) != hipSuccess)
-      return hipErrorInvalidConfiguration;
-    attr_set = true;
-  }
+  if (set_lds_limit(reinterpret_cast<const void*>(&k_gemm_nvfp4_px), kPxLds) != hipSuccess)
+    return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_gemm_nvfp4_px, dim3((unsigned)(tiles_m * tiles_n)), dim3(kNvThreads), kPxLds, s,
                      M, N, K, ac, as, aa, static_cast<const uint8_t*>(bx), ba,
                      static_cast<uint16_t*>(c), ldc, tiles_m, tiles_n, vec_store ? 1 : 0);

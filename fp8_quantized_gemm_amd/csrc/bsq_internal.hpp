@@ -11,6 +11,11 @@ enum Fmt { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2, kFP8 = 3 };   // kFP8: per-tensor
 // One-byte (E4M3) elements: MXFP8 and per-tensor FP8.
 constexpr bool fp8_elems(int f) { return f == kMXFP8 || f == kFP8; }
 
+// Raises the dynamic-LDS limit of kernel `fn` to `bytes` on the current
+// device, once per (device, kernel): later calls return the first call's
+// result.  Thread-safe (several host threads may launch at once).
+hipError_t set_lds_limit(const void* fn, int bytes);
+
 // Sets *a = 0 and *b = 0 (either may be null).
 hipError_t launch_zero_amax(float* a, float* b, hipStream_t s);
 // *dst = *src.

@@ -165,7 +165,10 @@ bsq_status quantize_transpose(const void* x, int64_t rows, int64_t cols, bsq_for
  *   block_rows, rnd, seed, offset, rht_col, rht_signs : as quantize_transpose.
  *   amax_row : in, device FP32 max|x|; required with the row outputs.
  *   amax_col : in, device FP32 amax of the col side (max|RHT(x^T)| with
- *              rht_col, else max|x|); required with the col outputs.
+ *              rht_col, else max|x|); required with the col outputs.  With
+ *              block_rows 16 and both orientations it must be the same
+ *              pointer as amax_row (one amax encodes both sides of a 16x16
+ *              tile); BSQ_EINVAL otherwise.
  *   codes_row, scales_row / codes_col, scales_col : out, as quantize_transpose;
  *              either pair may be NULL to skip that orientation (not both).
  * Requires rows % 16 == 0 and cols % 16 == 0.

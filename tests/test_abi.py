@@ -138,6 +138,8 @@ def test_quantize_transpose_amax_argument_errors():
     assert _qta(block_rows=16, rnd=1) == bsq.BSQ_EUNSUPPORTED
     assert _qta(block_rows=16, rht=1) == bsq.BSQ_EUNSUPPORTED
     assert _qta(rows=0) == bsq.BSQ_OK                     # empty: nothing to launch
+    # 16x16 tiles encode both sides under one amax: the same pointer for both
+    assert _qta(block_rows=16, ac=FAKE + 0x1000) == bsq.BSQ_EINVAL
 
 
 def _sw(rows=32, f=32, y=FAKE, h=FAKE + 0x100000, ar=None, ac=None, rht=0):
@@ -248,6 +250,52 @@ def test_binding_rejects_host_tensors():
     from fp8_quantized_gemm_amd.mlp import MLPLayer
     with pytest.raises(ValueError):
         MLPLayer(torch.zeros(32, 16), torch.zeros(16, 16), 16)
+
+
+def test_binding_checks_operand_shapes_before_any_launch():
+    """Wrong operand widths, dtypes or output shapes raise ValueError in the
+    binding (the C ABI sees raw pointers and cannot check buffer sizes); the
+    checks run before the device check, so host tensors exercise them."""
+    import torch
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    f32 = torch.zeros(1, dtype=torch.float32)
+    M, N, K = 32, 48, 64
+    a, sa, b, sb = u8(M, K // 2), u8(M, K // 16), u8(N, K // 2), u8(N, K // 16)
+    with pytest.raises(ValueError, match="B codes"):          # K wider than B's codes
+        bsq.bs_gemm("nvfp4", a, sa, u8(N, K // 4), sb, f32, f32, K=K)
+    with pytest.raises(ValueError, match="A codes"):          # explicit K beyond the codes
+        bsq.bs_gemm("nvfp4", a, sa, b, sb, f32, f32, K=2 * K)
+    with pytest.raises(ValueError, match="A scales"):         # scales narrower than K / 16
+        bsq.bs_gemm("nvfp4", a, u8(M, K // 32), b, sb, f32, f32)
+    with pytest.raises(ValueError, match="B scales"):         # MX scales are per 32
+        bsq.bs_gemm("mxfp4", a, u8(M, K // 32), b, sb)
+    with pytest.raises(ValueError, match="codes must be"):    # codes of the wrong dtype
+        bsq.bs_gemm("nvfp4", a.float(), sa, b, sb, f32, f32, K=K)
+    with pytest.raises(ValueError, match="amax"):             # NVFP4 needs both amaxes
+        bsq.bs_gemm("nvfp4", a, sa, b, sb, f32, None)
+    with pytest.raises(ValueError, match="amax"):             # amax of the wrong dtype
+        bsq.bs_gemm("nvfp4", a, sa, b, sb, f32, torch.zeros(1, dtype=torch.float64))
+    with pytest.raises(ValueError, match="out"):              # out with fewer rows than M
+        bsq.bs_gemm("nvfp4", a, sa, b, sb, f32, f32, out=torch.zeros(M - 1, N, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out"):              # out not bf16
+        bsq.bs_gemm("nvfp4", a, sa, b, sb, f32, f32, out=torch.zeros(M, N, dtype=torch.float16))
+    with pytest.raises(ValueError, match="A codes"):          # fp8 codes: one byte per element
+        bsq.bs_gemm("fp8", a, None, u8(N, K), None, f32, f32, K=K)
+    with pytest.raises(ValueError, match="unknown format"):
+        bsq.bs_gemm("nvfp8", a, sa, b, sb, f32, f32)
+    with pytest.raises(ValueError, match="expand scales"):
+        bsq.nvfp4_expand(b, u8(N, K // 32))
+    with pytest.raises(ValueError, match="out"):              # expansion output is fp16 [N, K]
+        bsq.nvfp4_expand(b, sb, out=torch.zeros(N, K, dtype=torch.bfloat16))
+    bx = torch.zeros(N, K, dtype=torch.float16)
+    with pytest.raises(ValueError, match="b_x"):
+        bsq.bs_gemm_nvfp4_bx(a, sa, f32, bx.bfloat16(), f32)
+    with pytest.raises(ValueError, match="A codes"):          # A narrower than B's K
+        bsq.bs_gemm_nvfp4_bx(u8(M, K // 4), sa, f32, bx, f32)
+    with pytest.raises(ValueError, match="out"):
+        bsq.bs_gemm_nvfp4_bx(a, sa, f32, bx, f32, out=torch.zeros(M, N + 1, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="CUDA"):             # right shapes, host memory
+        bsq.bs_gemm("nvfp4", a, sa, b, sb, f32, f32)
 
 
 def test_element_counts_beyond_2_48_are_rejected():

@@ -175,6 +175,11 @@ def test_quantize_transpose_amax_against_oracle(R, C, br, rnd, rht):
     ref = Q.quantize_transpose(bits(x), "nvfp4", br, rnd, seed, offset, rht, SIGNS)
     ar = torch.tensor([ref["row_amax"]], dtype=torch.float32, device="cuda")
     ac = torch.tensor([ref["col_amax"]], dtype=torch.float32, device="cuda")
+    if br == 16:       # 16x16 tiles: one amax for both sides, passed once
+        with pytest.raises(bsq.BsqError) as e:
+            bsq.quantize_transpose_amax(x, ar, ac, br, rnd, seed, offset, rht, SIGNS)
+        assert e.value.status == bsq.BSQ_EINVAL
+        ac = ar
     d = bsq.quantize_transpose_amax(x, ar, ac, br, rnd, seed, offset, rht, SIGNS)
     torch.cuda.synchronize()
     for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
@@ -186,7 +191,8 @@ def test_quantize_transpose_amax_matches_quantize_transpose(R, C, br, rnd, rht):
     announce("qt amax vs qt", R, C, br, rnd, rht)
     x = synth.bf16_tensor((R, C), 8500 + R + C, 1.0, br == 1, device="cuda")
     q = bsq.quantize_transpose(x, "nvfp4", br, rnd, 77, 5, rht, SIGNS)
-    d = bsq.quantize_transpose_amax(x, q["row_amax"], q["col_amax"], br, rnd, 77, 5, rht, SIGNS)
+    d = bsq.quantize_transpose_amax(x, q["row_amax"], q["row_amax"] if br == 16 else q["col_amax"],
+                                    br, rnd, 77, 5, rht, SIGNS)
     one_row = bsq.quantize_transpose_amax(x, q["row_amax"], None, br, rnd, 77, 5, rht, SIGNS, col=False)
     one_col = bsq.quantize_transpose_amax(x, None, q["col_amax"], br, rnd, 77, 5, rht, SIGNS, row=False)
     torch.cuda.synchronize()
