@@ -135,6 +135,41 @@ def test_sr_stream_map_words():
     assert abs(u.mean() / 65535 - 0.5) < 0.005
 
 
+def test_sr_decisions_follow_an_independent_philox():
+    """End to end through the oracle's SR quantizer: MXFP4 blocks [4, 0.25 x 31]
+    have block exponent 0, so every 0.25 sits exactly halfway between E2M1
+    magnitudes 0 and 0.5 and rounds up iff its 16-bit word is below 2^15.
+    The expected decisions come from rocRAND's installed Philox4x32-10 engine
+    (not the oracle's generator): element idx of a rowwise output uses the
+    16-bit half (idx & 1) of word (idx & 7) >> 1 of the call at counter
+    (idx >> 3, offset, stream)."""
+    exe = _build_rocrand_helper()
+    if exe is None:
+        pytest.skip("rocRAND headers / hipcc not available: SR cross-check skipped")
+    R, C, seed, offset = 6, 64, 0xA5A5123456, 7
+    x = np.full((R, C), 0.25, dtype=np.float32)
+    x[:, ::32] = 4.0
+    codes, scales = Q.mx_quantize(x, "mxfp4", "sr", seed, offset)
+    assert np.all(scales == 127)
+    got = F.unpack_e2m1(codes).reshape(R, C)
+    groups = R * C // 8
+    inp = "".join(f"{seed} {g} 0 {offset} 0\n" for g in range(groups))
+    out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+    words = np.array([[int(v) for v in ln.split()] for ln in out.strip().split("\n")], dtype=np.uint64)
+    idx = np.arange(R * C)
+    w = words[idx >> 3, (idx & 7) >> 1]
+    r16 = (w >> (16 * (idx & 1)).astype(np.uint64)) & np.uint64(0xFFFF)
+    want = np.where(r16 < 0x8000, 1, 0).reshape(R, C)          # E2M1 code 1 = 0.5
+    want[:, ::32] = 6                                          # 4.0 is on the grid
+    assert np.array_equal(got, want)
+    # row-major global index: the same values as one row give the same codes,
+    # the column stream (1) gives different ones
+    flat, _ = Q.mx_quantize(x.reshape(1, R * C), "mxfp4", "sr", seed, offset)
+    assert np.array_equal(flat.reshape(codes.shape), codes)
+    other, _ = Q.mx_quantize(x, "mxfp4", "sr", seed, offset, stream=1)
+    assert not np.array_equal(other, codes)
+
+
 # ---------------------------------------------------------------- GEMM
 
 E2M1_TAB = [Fraction(v) for v in ("0", "1/2", "1", "3/2", "2", "3", "4", "6")]
