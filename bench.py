@@ -478,20 +478,26 @@ def mlp_layer_step(step, steps, warmup, rel_update=1e-4):
 
 
 def route_ceilings(device, iters=4000, blocks=1024):
-    """Inner-loop ceilings of the two exact NVFP4 GEMM routes (operands in
-    registers, no memory): route (a), a per-16-K FP16 MFMA on unscaled E2M1
-    values plus the VALU rescale acc += sA * sB * P, against route (b)'s same
-    MFMAs accumulating directly.  Two timed launches each (HIP events on the
-    launch stream), the second reported."""
+    """Inner-loop ceilings of the exact NVFP4 GEMM routes (operands in
+    registers, no memory): route (a), a per-16-K MFMA on unscaled E2M1 values
+    plus the VALU rescale acc += sA * sB * P, on the FP16 32x32x16 MFMA and on
+    the scaled FP4 32x32x64 MFMA (one 16-block per instruction); route (b)'s
+    FP16 MFMAs accumulating directly; and the scaled FP4 MFMA accumulating
+    directly over all 64 K positions (the MXFP4 instruction's own ceiling).
+    Useful flops only (a 16-block per route-(a) instruction).  Two timed
+    launches each (HIP events on the launch stream), the second reported."""
     path = os.path.join(ROOT, "fp8_quantized_gemm_amd", "libbsq_ceiling.so")
     L = ctypes.CDLL(path)
     L.bsq_route_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.bsq_route_ceiling.restype = ctypes.c_int
     stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
     sink = torch.zeros(blocks * 512, dtype=torch.float32, device=device)
-    flops = blocks * 8 * iters * 8 * 2.0 * 32 * 32 * 16
+    flops16 = blocks * 8 * iters * 8 * 2.0 * 32 * 32 * 16
     out = {}
-    for mode, key in ((1, "route_b_mfma_only"), (0, "route_a_mfma_plus_valu_rescale")):
+    for mode, key, kmul, peak in ((1, "route_b_fp16_mfma_only", 1, PEAK_FP16_TFLOPS),
+                                  (0, "route_a_fp16_mfma_plus_valu_rescale", 1, PEAK_FP16_TFLOPS),
+                                  (2, "route_a_scaled_fp4_mfma_plus_valu_rescale", 1, PEAK_FP16_TFLOPS),
+                                  (3, "mxfp4_scaled_mfma_only", 4, PEAK_FP4_TFLOPS)):
         for _ in range(2):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -500,9 +506,13 @@ def route_ceilings(device, iters=4000, blocks=1024):
             assert st == 0, st
             torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        out[key] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
-    out["note"] = ("FP16 MFMA loops with operands in registers; the complete route (b) GEMM "
-                   "(roofline.achieved) includes all memory traffic and the expansion")
+        tf = flops16 * kmul / (ms * 1e-3) / 1e12
+        out[key] = {"ms": round(ms, 3), "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4),
+                    "peak_tflops": peak}
+    out["note"] = ("MFMA loops with operands in registers; route (a) counts the 16-block's flops "
+                   "(the scaled FP4 instruction runs 64 K positions, 48 of them zero); the "
+                   "complete route (b) GEMM (roofline.achieved) includes all memory traffic and "
+                   "the expansion")
     return out
 
 
@@ -708,6 +718,8 @@ def main():
     ap.add_argument("--no-405b", action="store_true",
                     help="skip the Llama-3.1-405B layer summary of the default (8B) run")
     ap.add_argument("--no-tiny", action="store_true", help="skip the 256^3 FPROP record")
+    ap.add_argument("--only", choices=["route-ceilings", "mx-square"],
+                    help="run one auxiliary leg alone and print its JSON (for counter profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path "
@@ -716,6 +728,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        leg = {"route-ceilings": route_ceilings, "mx-square": mx_square}[args.only]
+        print(json.dumps({args.only: leg(dev)}))
+        return
     flush = Flusher(dev)
     step, ms_list, per, wall = run_step_bench(args.workload, not args.no_rht, dev, args.steps,
                                               args.warmup, flush, bx=not args.no_bx)
