@@ -760,8 +760,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "nvfp4 (e2m1 x e4m3 blocks) -> exact fp16 expansion, fp16 mfma, fp32 accumulate, bf16 out",
-        "data": "synthetic (seeded N(0,1)+0.1% x50 outliers activations, N(0,0.02^2) weights, "
-                "N(0,1e-3^2) gradients)",
+        "data": ("synthetic (seeded N(0,1)+0.1% x50 outliers activations, N(0,0.02^2) weights, "
+                 "N(0,1e-3^2) gradients)" if args.workload == "8b" else
+                 "synthetic (seeded N(0,1)+0.1% x50 outliers activations and gradients, N(0,0.01^2) weights)"),
         "config": {"workload": f"llama3-{args.workload} MLP layer FPROP+DGRAD+WGRAD, one GPU share",
                    "tokens": step.dims["tokens"], "hidden": step.dims["hidden"],
                    "ffn": step.dims["ffn"], "rht": not args.no_rht,
