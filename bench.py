@@ -12,7 +12,7 @@ One step = the whole hot path of one transformer-MLP layer on one GPU's share
           GEMM dW_gu = dY_gu^T . X
 value = sum(2 M N K) / step time, with BF16 inputs already resident in HBM;
 the step time is the median over the timed steps (HIP events on the launch
-stream), with a 1 GiB scratch write between steps so that no step starts
+stream), with a 1 GiB scratch read between steps so that no step starts
 with its inputs in the 256 MB MALL.
 
 Also reported, each in its own field:
@@ -73,18 +73,19 @@ FLUSH_BYTES = 1 << 30
 
 
 class Flusher:
-    """Writes a 1 GiB scratch buffer between timed repetitions, so that no
+    """Reads a 1 GiB scratch buffer between timed repetitions, so that no
     repetition finds its inputs in the 256 MB MALL or the L2s left warm by
     the previous one (the per-tensor amax passes would otherwise be
-    flattered)."""
+    flattered).  A read, not a write: the lines it leaves behind are clean,
+    so the next repetition's first kernel does not share HBM with the
+    write-back of the flush itself (the previous repetition's dirty lines are
+    written back during the flush)."""
 
     def __init__(self, device):
-        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
-        self.k = 0
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
 
     def __call__(self):
-        self.k += 1
-        self.buf.fill_(self.k)
+        torch.sum(self.buf, dtype=torch.int64)
 
 
 def median(v):
@@ -769,7 +770,7 @@ def main():
                    "step_tflop": round(step.flops / 1e12, 3),
                    "pct_of_fp16_mfma_peak": round(100 * value / PEAK_FP16_TFLOPS, 2)},
         "timing": (f"median of {args.steps} steps (HIP events on the launch stream), a 1 GiB "
-                   f"scratch write between steps; mean {sum(ms_list) / len(ms_list):.4f} ms"),
+                   f"scratch read between steps; mean {sum(ms_list) / len(ms_list):.4f} ms"),
         "roofline": {"bound": "mfma", "kernel": ("NVFP4 GEMM, 6 launches per step: k_gemm_nvfp4_pp, and "
                                                  "k_gemm_nvfp4_px for " + (", ".join(n for n, v in step.bx.items() if v) or "none")),
                      "achieved": round(gemm_tflops, 1), "peak": PEAK_FP16_TFLOPS,
