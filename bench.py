@@ -771,8 +771,8 @@ def main():
                    "pct_of_fp16_mfma_peak": round(100 * value / PEAK_FP16_TFLOPS, 2)},
         "timing": (f"median of {args.steps} steps (HIP events on the launch stream), a 1 GiB "
                    f"scratch read between steps; mean {sum(ms_list) / len(ms_list):.4f} ms"),
-        "roofline": {"bound": "mfma", "kernel": ("NVFP4 GEMM, 6 launches per step: k_gemm_nvfp4_pp, and "
-                                                 "k_gemm_nvfp4_px for " + (", ".join(n for n, v in step.bx.items() if v) or "none")),
+        "roofline": {"bound": "mfma", "kernel": ("NVFP4 GEMM, 6 launches per step: k_gemm_nvfp4_rx" +
+                                                 "".join(f"; k_gemm_nvfp4_px for {n}" for n, v in step.bx.items() if v)),
                      "achieved": round(gemm_tflops, 1), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": gemm_traffic(args.workload),

@@ -336,15 +336,19 @@ def bs_gemm(fmt, a_codes, a_scales, b_codes, b_scales, a_amax=None, b_amax=None,
     return out
 
 
-BX_MAX_BYTES = 128 << 20
+# Largest FP16 B operand worth pre-expanding.  Zero: since the register-
+# expansion GEMM (K % 256 == 0) expands in the tile faster than the
+# pre-expanded-B kernel streams FP16, no Llama MLP GEMM gains from it
+# (measured in the 8B step: FPROP_down 1549 against 1345 TF/s, DGRAD_down
+# 1437 against 1264).  bs_gemm_nvfp4_bx stays available for callers that keep
+# an expanded weight anyway.
+BX_MAX_BYTES = 0
 
 
 def bx_pays(N, K):
     """Whether a GEMM should take its B operand pre-expanded (nvfp4_expand +
     bs_gemm_nvfp4_bx) rather than expand it inside every output tile: when the
-    FP16 copy of B stays cache-resident (at most 128 MiB).  Measured on the
-    Llama 3 8B MLP GEMMs: +2-9% where B is W_down (117 MB as FP16), 0 to -3%
-    where B is larger (W_gu, X^T, H^T: 235-940 MB)."""
+    FP16 copy of B is at most BX_MAX_BYTES (see there; currently never)."""
     return N * K * 2 <= BX_MAX_BYTES and K % 128 == 0
 
 

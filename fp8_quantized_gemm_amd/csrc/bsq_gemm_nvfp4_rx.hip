@@ -1,0 +1,470 @@
+// NVFP4 block-scaled GEMM for gfx950, register-expansion schedule:
+// C[M, N] (BF16) = alpha * A[M, K] . B[N, K]^T, A and B packed E2M1 codes with
+// one E4M3 scale per 16 K-elements and a per-tensor FP32 scale each.
+//
+// NVFP4 pretraining post, data-flow paragraph after Figure 1: FPROP, DGRAD and
+// WGRAD consume NVFP4 operands and emit BF16; recipe ingredients 1-2 define
+// the operand format.  E2M1 x E4M3 is exact in FP16, so every operand element
+// is expanded exactly to FP16 (v * S * 2^-7) and fed to the FP16 MFMA.
+//
+// Work split: one 256-thread workgroup (four waves, one per SIMD) per 256 x 256
+// output tile; wave w owns the 128 x 128 quarter (w >> 1, w & 1) and keeps it
+// as 8 x 8 accumulator tiles of 16 x 16 (v_mfma_f32_16x16x32_f16, 256 FP32
+// accumulator registers pinned by inline assembly).
+//
+// Why registers and not LDS for the FP16 values: expanding each operand once
+// per workgroup into LDS and reading FP16 fragments back costs more LDS
+// traffic per MFMA than the LDS can serve at the MFMA rate.  Here each wave
+// reads the packed codes (4 bits per element) and block scales of its own 128
+// A rows and 128 B rows from LDS and expands them in registers, interleaved
+// with its MFMAs.  Every A row is expanded by the two waves that share it
+// (likewise B): two VALU operations per MFMA, and a quarter of the LDS
+// traffic of FP16 fragments.
+//
+// K layout inside a 128-element unit of K: lane group g = lane >> 4 owns the
+// 32 elements [32 g, 32 g + 32) of its row (16 code bytes, two block scales),
+// and MFMA step ks (0..3) of the unit feeds it elements 32 g + 8 ks .. + 7.
+// A and B use the same map, so each step contracts a quarter of the unit and
+// the four steps together all of it (the sum over K is order-free; the
+// accumulation order differs from a natural-order K walk only in FP32
+// rounding).
+//
+// Pipeline per unit U (four steps of 64 MFMAs):
+//  * raw units reach LDS by global -> LDS direct loads (per row 64 code bytes
+//    as four 16-byte chunks, and 8 scale bytes), four unit buffers, units
+//    issued three ahead; wave w loads A rows and B rows 64 w .. 64 w + 63,
+//    its 12 loads spread over the unit's 256 MFMAs (one every 21) rather
+//    than issued in one burst; one workgroup barrier per unit makes a
+//    landed unit visible to all waves and retires the buffer the unit three
+//    ahead will fill;
+//  * each tile's 16 code bytes for the unit (its four steps) are read from
+//    LDS in one piece, as soon as the previous unit's last expansion from
+//    them is done, about a step ahead of their first use; the scales of
+//    U + 1 during step 2;
+//  * during step ks: B tile n of step ks is expanded just in time (during the
+//    MFMAs of B tile n - 1), and the eight A tiles and first two B tiles of
+//    step ks + 1 are expanded for the next step.
+// Fragments are written by VALU operations and read by MFMAs written as
+// inline assembly, so the compiler's hazard recognizer does not see those
+// dependencies: every fragment is complete at least one MFMA before its first
+// reader, and explicit s_nop cover the register copies at step boundaries.
+// LDS code rows are 64 bytes: the 16-byte chunk c of row r sits at slot
+// c ^ swz(r), swz(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1).  A 16-byte read is
+// served eight lanes at a time by 32 four-byte banks; the eight lanes (eight
+// consecutive rows, one lane group) then touch 32 distinct banks.
+#include "bsq_gemm_common.hpp"
+#include "bsq_internal.hpp"
+
+namespace bsq {
+
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRxThreads = 256;
+constexpr int kRxCodeB = 256 * 64;                      // one operand's codes of a 128-K unit
+constexpr int kRxOpB = kRxCodeB + 256 * 8;              // plus its scales: 18 KiB
+constexpr int kRxUnitB = 2 * kRxOpB;                    // A then B: 36 KiB
+constexpr int kRxNBuf = 4;                              // raw unit buffers
+constexpr int kRxLds = kRxNBuf * kRxUnitB;              // 147456
+constexpr int kRxEpiRowB = 272;                         // epilogue: 128 BF16 + 16 bytes pad per row
+constexpr int kRxLoadsPerUnit = 12;                     // direct loads per wave and unit
+static_assert(2 * kRxLoadsPerUnit <= 63, "the wait counts of two units fit the load counter");
+static_assert(4 * 128 * kRxEpiRowB <= kRxLds, "epilogue staging must fit");
+static_assert(kRxLds <= 160 * 1024, "LDS plan");
+
+__host__ __device__ constexpr int rx_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+// Where the operands come from (all wave-uniform).
+struct RxSrc {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  uint32_t m0, n0, last_m, last_n;     // tile origin; last valid row of each operand
+  uint32_t code_ld, scale_ld;          // bytes per operand row
+};
+
+// Direct loads of raw unit `u` (K elements 128 u .. 128 u + 127) of A rows and
+// B rows 64 w .. 64 w + 63 of the tile into the unit buffer at LDS address
+// `raw`, load Q (0..11) of 12: Q / 6 picks the operand; Q % 6 < 4 is a code
+// load of 16 rows x 64 bytes, one 16-byte chunk per lane (lane l fills row
+// l >> 2, slot l & 3 of the 16 rows with the chunk that belongs there);
+// 4-5 a scale load of 32 rows x 8 bytes.  Rows past the operand re-read its
+// last row (their results are never stored).  32-bit offsets: operands are
+// below 4 GiB.
+template <int Q>
+__device__ __forceinline__ void rx_stage_one(const RxSrc& s, uint32_t u, uint32_t raw, int w, int lane) {
+  constexpr int op = Q / 6, i = Q % 6;
+  const uint32_t base = op ? s.n0 : s.m0, last = op ? s.last_n : s.last_m;
+  const uint32_t dst = raw + (uint32_t)(op * kRxOpB);
+  if constexpr (i < 4) {
+    const uint8_t* cq = (op ? s.b_codes : s.a_codes) + u * 64;
+    const int rr = i * 16 + (lane >> 2);                 // row within the wave's 64
+    const int c = (lane & 3) ^ rx_swz(rr);               // chunk held at slot lane & 3
+    const uint32_t gr = min(base + (uint32_t)(w * 64 + rr), last);
+    dma_to_lds<16>(cq, gr * s.code_ld + (uint32_t)(c * 16), dst + (uint32_t)((w * 64 + i * 16) * 64));
+  } else {
+    const uint8_t* sq = (op ? s.b_scales : s.a_scales) + u * 8;
+    const uint32_t gr = min(base + (uint32_t)(w * 64 + (i - 4) * 32 + (lane >> 1)), last);
+    dma_to_lds<4>(sq, gr * s.scale_ld + (uint32_t)(lane & 1) * 4,
+                  dst + (uint32_t)(kRxCodeB + (w * 64 + (i - 4) * 32) * 8));
+  }
+}
+
+// All 12 loads of a unit at once (prologue).
+template <int Q = 0>
+__device__ __forceinline__ void rx_stage(const RxSrc& s, uint32_t u, uint32_t raw, int w, int lane) {
+  if constexpr (Q < 12) {
+    rx_stage_one<Q>(s, u, raw, w, lane);
+    rx_stage<Q + 1>(s, u, raw, w, lane);
+  }
+}
+
+// Where in a unit (slot 64 ks + k of its 256) the 12 loads of the unit three
+// ahead are issued: load Q at slot 21 Q + 10, spread out so that no slot
+// waits for a burst of loads to be accepted.
+__host__ __device__ constexpr int rx_ld_at(int KS, int K) {
+  const int x = KS * 64 + K - 10;
+  return (x >= 0 && x % 21 == 0 && x / 21 < 12) ? x / 21 : -1;
+}
+
+struct RxLd {
+  const RxSrc* s;
+  uint32_t u, raw;     // unit to load and its buffer
+  int w, lane;
+};
+
+// acc += srcA . srcB on the FP16 MFMA (16 x 16 output, K = 32), written out so
+// that each accumulator tile keeps one fixed quad of accumulator registers for
+// the whole kernel (tied input / output).  The operands are written by VALU
+// operations at least one MFMA earlier.
+__device__ __forceinline__ void rx_mfma(floatx4& acc, const halfx8& a, const halfx8& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Per-lane LDS offsets, fixed for the kernel: tile T (0-7 A tiles of the
+// wave's rows, 8-15 B tiles of its columns) adds (T & 7) * 1024 to the code
+// offsets and (T & 7) * 128 to the scale offsets (16 rows per tile).
+struct RxLane {
+  int ca, cb;          // chunk g of row (lane & 15) of A / B tile 0 (16 bytes: the four steps)
+  int sa, sb;          // the two scale bytes 2 g, 2 g + 1 of those rows
+};
+
+// Registers of the pipeline (indices are compile-time after unrolling).  The
+// code dword of tile T for step ks sits in cw[T][ks]: the tile's 16 code
+// bytes of one unit, read from LDS in one piece (see rx_reads).
+struct RxRegs {
+  uint32_t cw[16][4];        // code dwords (8 E2M1 codes) per tile and step
+  uint32_t sraw[16];         // scale bytes 2 g, 2 g + 1 of the next unit, as read
+  halfx2 pr[2][16];          // {S(2g), S(2g + 1)} * 2^7 per tile, units of parity 0 / 1
+  halfx8 a[2][8];            // A fragments of the current step and the next
+  halfx8 b[8];               // B fragments of the current step
+  halfx8 nb[2];              // first two B fragments of the next step
+  uint32_t o[3][4];          // pairs of the fragment being expanded, per stream:
+                             // A tiles of the next step, B tile of this step, B tiles 0-1 of the next
+};
+
+// Pair SEL (0-3) of the expansion of tile T for step s (= KS of a unit of
+// parity UP): byte SEL of the step's code dword times the block scale of the
+// step (block 2 g for steps 0-1, 2 g + 1 for steps 2-3), see dequant8.
+template <int UP, int KS, int T, int SEL>
+__device__ __forceinline__ uint32_t rx_pk(const RxRegs& r) {
+  const halfx2 p = r.pr[UP][T];
+  const halfx2 s = (KS >> 1) ? halfx2{p.y, p.y} : halfx2{p.x, p.x};
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.cw[T][KS], 0x1p-14f, SEL) * s);
+}
+
+template <int UP, int KS, int T, int SEL, int STREAM>
+__device__ __forceinline__ void rx_pair_to(RxRegs& r, halfx8& dst) {
+  uint32_t (&o)[4] = r.o[STREAM];
+  o[SEL] = rx_pk<UP, KS, T, SEL>(r);
+  if constexpr (SEL == 3) dst = __builtin_bit_cast(halfx8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// The A pairs of step ks + 1 go after steps rx_aq(q) (q = 0..31), spread over
+// steps 0..55; the B pairs of tile n (2..7) of step ks after steps
+// 8 (n - 1) + 0, 2, 4, 6; those of tiles 0 and 1 of step ks + 1 after steps
+// 56..63.
+__host__ __device__ constexpr int rx_aq(int q) { return (q * 55) / 31; }
+
+template <int UP, int KS, int K, int Q>
+__device__ __forceinline__ void rx_a_pairs(RxRegs& r) {
+  if constexpr (Q < 32) {
+    if constexpr (rx_aq(Q) == K) {
+      // step KS + 1 of this unit, or step 0 of the next (parity UP ^ 1)
+      constexpr int NKS = (KS + 1) & 3, NUP = KS == 3 ? (UP ^ 1) : UP;
+      rx_pair_to<NUP, NKS, (Q >> 2), (Q & 3), 0>(r, r.a[(KS + 1) & 1][Q >> 2]);
+    }
+    rx_a_pairs<UP, KS, K, Q + 1>(r);
+  }
+}
+
+// LDS reads of step KS (after step K).  A tile's 16 code bytes (its four
+// steps of the unit) are read in one piece into cw[T] as soon as the current
+// unit's last expansion from them is done: A tiles after their last pair of
+// step 2 (for step 3), B tiles 0-1 after theirs (step 2, slots 59 and 63),
+// B tiles 2-7 after their just-in-time pairs of step 3; each about 57 steps
+// before the next unit's first expansion from them.  In step 2, the scale
+// bytes of the next unit (steps 1, 3, .., 31).
+__host__ __device__ constexpr int rx_cread(int KS, int K) {
+  if (KS == 2) {
+    for (int T = 0; T < 8; ++T)
+      if (K == (4 * T + 3) * 55 / 31 + 1) return T;
+    if (K == 60) return 8;
+  }
+  if (KS == 3) {
+    if (K == 0) return 9;
+    if (K % 8 == 7 && K >= 15 && K <= 55) return 8 + (K + 1) / 8;
+  }
+  return -1;
+}
+template <int KS, int K>
+__device__ __forceinline__ void rx_reads(RxRegs& r, const uint8_t* ucur, const uint8_t* unxt,
+                                         const RxLane& ln) {
+  if constexpr (rx_cread(KS, K) >= 0) {
+    constexpr int T = rx_cread(KS, K);
+    const uint4 q = *reinterpret_cast<const uint4*>(unxt + (T < 8 ? ln.ca : ln.cb) + (T & 7) * 1024);
+    r.cw[T][0] = q.x;
+    r.cw[T][1] = q.y;
+    r.cw[T][2] = q.z;
+    r.cw[T][3] = q.w;
+  }
+  if constexpr (KS == 2 && (K & 1) == 1 && K < 32) {
+    constexpr int T = K >> 1;
+    r.sraw[T] = *reinterpret_cast<const uint16_t*>(unxt + (T < 8 ? ln.sa : ln.sb) + (T & 7) * 128);
+  }
+}
+
+// Step K (0..63) of step KS of a unit of parity UP: MFMA K (B tile K >> 3 x A
+// tile K & 7), then the work placed after it.
+template <int UP, bool LOADS, int KS, int K>
+__device__ __forceinline__ void rx_step(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* ucur,
+                                        const uint8_t* unxt, const RxLane& ln, const RxLd& ld) {
+  constexpr int n = K >> 3, mi = K & 7;
+  rx_mfma(acc[mi][n], r.b[n], r.a[KS & 1][mi]);
+  if constexpr (LOADS && rx_ld_at(KS, K) >= 0) rx_stage_one<rx_ld_at(KS, K)>(*ld.s, ld.u, ld.raw, ld.w, ld.lane);
+  // B tile n + 1 of this step, just in time (its last pair one MFMA before
+  // the MFMA that reads it: a VALU write needs wait states before an MFMA
+  // reads the register, and the compiler does not see into the MFMA asm)
+  if constexpr ((K & 1) == 0 && n + 1 >= 2 && n + 1 < 8)
+    rx_pair_to<UP, KS, (8 + n + 1), ((K & 7) >> 1), 1>(r, r.b[n + 1]);
+  // A tiles of the next step
+  rx_a_pairs<UP, KS, K, 0>(r);
+  // B tiles 0 and 1 of the next step
+  if constexpr (K >= 56) {
+    constexpr int NKS = (KS + 1) & 3, NUP = KS == 3 ? (UP ^ 1) : UP, q = K - 56;
+    rx_pair_to<NUP, NKS, (8 + (q >> 2)), (q & 3), 2>(r, r.nb[q >> 2]);
+  }
+  rx_reads<KS, K>(r, ucur, unxt, ln);
+  // the next unit's scale pairs, 16 steps after their reads
+  if constexpr (KS == 2 && K >= 34 && K < 50)
+    r.pr[UP ^ 1][K - 34] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sraw[K - 34], 128.0f, false);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int UP, bool LOADS, int KS, int K>
+__device__ __forceinline__ void rx_steps(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* ucur,
+                                         const uint8_t* unxt, const RxLane& ln, const RxLd& ld) {
+  if constexpr (K < 64) {
+    rx_step<UP, LOADS, KS, K>(acc, r, ucur, unxt, ln, ld);
+    rx_steps<UP, LOADS, KS, K + 1>(acc, r, ucur, unxt, ln, ld);
+  }
+}
+
+template <int UP, bool LOADS, int KS>
+__device__ __forceinline__ void rx_kstep(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* ucur,
+                                         const uint8_t* unxt, const RxLane& ln, const RxLd& ld) {
+  rx_steps<UP, LOADS, KS, 0>(acc, r, ucur, unxt, ln, ld);
+  r.b[0] = r.nb[0];
+  r.b[1] = r.nb[1];
+  // wait states between these VALU copies and the next step's first MFMA
+  asm volatile("s_nop 4" ::: "memory");
+}
+
+// Unit U (parity UP): make unit U + 1 visible to every wave (this wave's own
+// loads of it waited for, then a barrier, which also means every wave has
+// finished reading unit U - 1), then the four steps, which (LOADS: unless
+// U + 3 is past the last unit) issue unit U + 3 into the buffer of unit U - 1
+// on the way.  Past the last unit, the next-unit reads fetch the last unit
+// again (its buffer is never refilled), which keeps the steps branch-free.
+template <int UP, bool LOADS>
+__device__ __forceinline__ void rx_unit(floatx4 (&acc)[8][8], RxRegs& r, uint8_t* smem,
+                                        uint32_t smem_lds, const RxSrc& s, int U, int NU, int w,
+                                        int lane, const RxLane& ln) {
+  if (U + 2 < NU) wait_vmcnt<kRxLoadsPerUnit>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+  RxLd ld;
+  ld.s = &s;
+  ld.u = (uint32_t)(U + 3);
+  ld.raw = smem_lds + (uint32_t)(((U + 3) & 3) * kRxUnitB);
+  ld.w = w;
+  ld.lane = lane;
+  const uint8_t* ucur = smem + (U & 3) * kRxUnitB;
+  const uint8_t* unxt = smem + ((U + 1 < NU ? U + 1 : NU - 1) & 3) * kRxUnitB;
+  // the VALU writes of the fragments expanded last need a few wait states
+  // before an MFMA reads them (the compiler does not track hazards into
+  // inline assembly)
+  asm volatile("s_nop 4" ::: "memory");
+  rx_kstep<UP, LOADS, 0>(acc, r, ucur, unxt, ln, ld);
+  rx_kstep<UP, LOADS, 1>(acc, r, ucur, unxt, ln, ld);
+  rx_kstep<UP, LOADS, 2>(acc, r, ucur, unxt, ln, ld);
+  rx_kstep<UP, LOADS, 3>(acc, r, ucur, unxt, ln, ld);
+}
+
+// Expansion of the A tiles (into a[0]) and the first two B tiles (into b) of
+// step 0 of unit 0 (prologue), from cw[T][0] and pr[0].
+template <int T>
+__device__ __forceinline__ void rx_prologue_tiles(RxRegs& r) {
+  if constexpr (T < 10) {
+    halfx8& d = T < 8 ? r.a[0][T & 7] : r.b[T & 7];
+    rx_pair_to<0, 0, T, 0, 0>(r, d);
+    rx_pair_to<0, 0, T, 1, 0>(r, d);
+    rx_pair_to<0, 0, T, 2, 0>(r, d);
+    rx_pair_to<0, 0, T, 3, 0>(r, d);
+    rx_prologue_tiles<T + 1>(r);
+  }
+}
+
+__global__ __launch_bounds__(kRxThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                     const uint8_t* a_scales, const float* __restrict__ a_amax,
+                     const uint8_t* b_codes, const uint8_t* b_scales,
+                     const float* __restrict__ b_amax, uint16_t* __restrict__ c, int64_t ldc,
+                     int tiles_m, int tiles_n, int vec_store) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  RxSrc s;
+  s.a_codes = a_codes;
+  s.a_scales = a_scales;
+  s.b_codes = b_codes;
+  s.b_scales = b_scales;
+  s.m0 = (uint32_t)tm * 256u;
+  s.n0 = (uint32_t)tn * 256u;
+  s.last_m = (uint32_t)(M - 1);
+  s.last_n = (uint32_t)(N - 1);
+  s.code_ld = (uint32_t)(K / 2);
+  s.scale_ld = (uint32_t)(K / 16);
+  const int NU = (int)(K / 128);
+  RxLane ln;
+  {
+    const int r16 = lane & 15, g = lane >> 4;
+    const int chunk = (g ^ rx_swz(r16)) << 4;            // rows 16 i + r16 share swz(r16)
+    ln.ca = (wm * 128 + r16) * 64 + chunk;
+    ln.cb = kRxOpB + (wn * 128 + r16) * 64 + chunk;
+    ln.sa = kRxCodeB + (wm * 128 + r16) * 8 + 2 * g;
+    ln.sb = kRxOpB + kRxCodeB + (wn * 128 + r16) * 8 + 2 * g;
+  }
+
+  floatx4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 8; ++jn) acc[i][jn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // prologue: units 0-2 in flight; unit 0's codes and scales in registers;
+  // the A tiles and first two B tiles of step 0 expanded
+  RxRegs r;
+  rx_stage(s, 0, smem_lds, w, lane);
+  if (NU > 1) rx_stage(s, 1, smem_lds + kRxUnitB, w, lane);
+  if (NU > 2) rx_stage(s, 2, smem_lds + 2 * kRxUnitB, w, lane);
+  // units 0 and 1 landed (at most one unit's loads still outstanding)
+  if (NU > 1) wait_vmcnt<kRxLoadsPerUnit>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+#pragma unroll
+  for (int T = 0; T < 16; ++T) {
+    const uint4 q = *reinterpret_cast<const uint4*>(smem + (T < 8 ? ln.ca : ln.cb) + (T & 7) * 1024);
+    r.cw[T][0] = q.x;
+    r.cw[T][1] = q.y;
+    r.cw[T][2] = q.z;
+    r.cw[T][3] = q.w;
+    r.pr[0][T] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+        *reinterpret_cast<const uint16_t*>(smem + (T < 8 ? ln.sa : ln.sb) + (T & 7) * 128), 128.0f, false);
+  }
+  rx_prologue_tiles<0>(r);
+
+  // units whose unit three ahead exists issue its loads; NU is even
+  int U = 0;
+  for (; U + 4 < NU; U += 2) {
+    rx_unit<0, true>(acc, r, smem, smem_lds, s, U, NU, w, lane, ln);
+    rx_unit<1, true>(acc, r, smem, smem_lds, s, U + 1, NU, w, lane, ln);
+  }
+  if (U + 3 < NU) {
+    rx_unit<0, true>(acc, r, smem, smem_lds, s, U, NU, w, lane, ln);
+    rx_unit<1, false>(acc, r, smem, smem_lds, s, U + 1, NU, w, lane, ln);
+    U += 2;
+  }
+  rx_unit<0, false>(acc, r, smem, smem_lds, s, U, NU, w, lane, ln);
+  rx_unit<1, false>(acc, r, smem, smem_lds, s, U + 1, NU, w, lane, ln);
+
+  // every wave is done with the unit buffers (the epilogue reuses the LDS),
+  // and the last MFMAs' results have reached the accumulator registers
+  lds_barrier();
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  // epilogue: alpha * acc -> BF16 (RNE), staged per wave through LDS so that
+  // global stores are 256-byte row segments.  acc[mi][ni] holds, in lane l,
+  // output row 16 mi + (l & 15) and columns 16 ni + 4 (l >> 4) + e of the
+  // wave's quarter.
+  const float alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax) * 16384.0f;
+  uint8_t* E = smem + w * (128 * kRxEpiRowB);
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) {
+      const floatx4 v = acc[mi][ni];
+      *reinterpret_cast<uint2*>(E + (mi * 16 + (lane & 15)) * kRxEpiRowB + (ni * 16 + (lane >> 4) * 4) * 2) =
+          make_uint2(pack_bf16x2(v[0] * alpha, v[1] * alpha), pack_bf16x2(v[2] * alpha, v[3] * alpha));
+    }
+  __syncthreads();
+  const int64_t gm0 = (int64_t)s.m0 + wm * 128, gn = (int64_t)s.n0 + wn * 128 + (lane & 15) * 8;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int row = it * 4 + (lane >> 4);
+    const int64_t gm = gm0 + row;
+    if (gm >= M) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(E + row * kRxEpiRowB + (lane & 15) * 16);
+    uint16_t* dst = c + gm * ldc + gn;
+    if (vec_store && gn + 7 < N) {
+      typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4n{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4n*>(dst));
+    } else {
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gn + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+}  // namespace
+
+bool gemm_nvfp4_rx_fits(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                        const uint8_t* bc, const uint8_t* bs) {
+  const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+  return K > 0 && K % 256 == 0 && al(ac, 16) && al(bc, 16) && al(as, 4) && al(bs, 4) &&
+         M * (K / 2) < ((int64_t)1 << 32) && N * (K / 2) < ((int64_t)1 << 32);
+}
+
+hipError_t launch_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                                const uint8_t* as, const float* aa, const uint8_t* bc,
+                                const uint8_t* bs, const float* ba, void* c, int64_t ldc,
+                                hipStream_t s) {
+  const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
+  const bool vec_store = (ldc % 8 == 0) && (reinterpret_cast<uintptr_t>(c) % 16 == 0);
+  if (set_lds_limit(reinterpret_cast<const void*>(&k_gemm_nvfp4_rx), kRxLds) != hipSuccess)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_gemm_nvfp4_rx, dim3((unsigned)(tiles_m * tiles_n)), dim3(kRxThreads), kRxLds,
+                     s, M, N, K, ac, as, aa, bc, bs, ba, static_cast<uint16_t*>(c), ldc, tiles_m,
+                     tiles_n, vec_store ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace bsq

@@ -70,6 +70,16 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                              const float* aa, const uint8_t* bc, const uint8_t* bs,
                              const float* ba, void* c, int64_t ldc, hipStream_t s);
 
+// The register-expansion NVFP4 GEMM (four waves, codes expanded in registers):
+// whether it takes these operands (K % 256 == 0, codes 16-byte and scales
+// 4-byte aligned, each operand below 4 GiB), and its launch.
+bool gemm_nvfp4_rx_fits(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                        const uint8_t* bc, const uint8_t* bs);
+hipError_t launch_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                                const uint8_t* as, const float* aa, const uint8_t* bc,
+                                const uint8_t* bs, const float* ba, void* c, int64_t ldc,
+                                hipStream_t s);
+
 // NVFP4 GEMM with B pre-expanded to FP16 (bx [N, K] = v * S * 2^-7, from
 // launch_nvfp4_expand).  hipErrorNotSupported unless K % 128 == 0, the
 // operands are 16-byte aligned (scales 4) and M * K / 2, N * K * 2 < 2^32.

@@ -51,7 +51,7 @@ def test_tiny_nvfp4_fprop_pipeline():
 
 @pytest.mark.parametrize("M", [16, 48, 256, 300])
 @pytest.mark.parametrize("N", [16, 48, 256, 272])
-@pytest.mark.parametrize("K", [32, 64, 128, 160, 4096])
+@pytest.mark.parametrize("K", [32, 64, 128, 160, 256, 384, 512, 4096])
 def test_nvfp4_shape_sweep(M, N, K):
     announce("nvfp4 sweep", M, N, K)
     A = synth.bf16_tensor((M, K), 1000 + M + K, device="cuda")
