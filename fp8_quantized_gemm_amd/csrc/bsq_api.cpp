@@ -27,6 +27,20 @@ hipError_t set_lds_limit(const void* fn, int bytes) {
   return r;
 }
 
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cus;   // device -> compute units
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cus.find(dev);
+  if (it != cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  cus.emplace(dev, n);
+  return n;
+}
+
 }  // namespace bsq
 
 namespace {
@@ -325,7 +339,7 @@ bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_
                      : fmt == BSQ_MXFP4 ? bsq::kMXFP4
                      : fmt == BSQ_MXFP8 ? bsq::kMXFP8 : bsq::kFP8;
   return hip_status(bsq::launch_gemm(f, M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales,
-                                     b_amax, c, ldc, static_cast<hipStream_t>(stream)));
+                                     b_amax, c, ldc, nullptr, 0, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

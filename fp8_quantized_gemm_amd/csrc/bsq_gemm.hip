@@ -618,11 +618,11 @@ hipError_t launch_gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
 hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,
-                       hipStream_t s) {
+                       void* scratch, size_t scratch_bytes, hipStream_t s) {
   switch (fmt) {
     case kNVFP4:
       return launch_gemm_nvfp4(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax, c,
-                               ldc, s);
+                               ldc, scratch, scratch_bytes, s);
     case kMXFP4:
       return launch_gemm_t<kMXFP4>(M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax,
                                    c, ldc, s);

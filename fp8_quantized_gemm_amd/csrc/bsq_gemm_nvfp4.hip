@@ -748,9 +748,28 @@ __global__ __launch_bounds__(256) void k_nvfp4_expand(const uint2* __restrict__ 
 
 hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                              const float* aa, const uint8_t* bc, const uint8_t* bs,
-                             const float* ba, void* c, int64_t ldc, hipStream_t s) {
+                             const float* ba, void* c, int64_t ldc, void* scratch,
+                             size_t scratch_bytes, hipStream_t s) {
   const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
   const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+  // the register-expansion kernel where it applies (13-14% faster on the
+  // Llama MLP shapes), its last wave split over K when it would leave more
+  // than half the compute units idle; the ping-pong kernel for K % 256 == 128
+  if (gemm_nvfp4_rx_fits(M, N, K, ac, as, bc, bs)) {
+    const int tail = gemm_nvfp4_rx_split(M, N, K, device_cus());
+    if (tail == 0) return launch_gemm_nvfp4_rx(M, N, K, ac, as, aa, bc, bs, ba, c, ldc, 0, nullptr, s);
+    const size_t bytes = (size_t)tail * kRxSplitTileBytes;
+    if (scratch != nullptr) {
+      if (scratch_bytes < bytes) return hipErrorInvalidValue;
+      return launch_gemm_nvfp4_rx(M, N, K, ac, as, aa, bc, bs, ba, c, ldc, tail, scratch, s);
+    }
+    void* part = nullptr;
+    hipError_t e = hipMallocAsync(&part, bytes, s);
+    if (e != hipSuccess) return e;
+    e = launch_gemm_nvfp4_rx(M, N, K, ac, as, aa, bc, bs, ba, c, ldc, tail, part, s);
+    const hipError_t f = hipFreeAsync(part, s);
+    return e != hipSuccess ? e : f;
+  }
   // the ping-pong kernel stages 64 code bytes and 8 scale bytes per row and four
   // half-stages, runs its loop in groups of four half-stages, and addresses
   // each operand with 32-bit byte offsets
@@ -762,10 +781,6 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
     return hipErrorInvalidConfiguration;
   uint16_t* cp = static_cast<uint16_t*>(c);
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kNvThreads);
-  // the register-expansion kernel where it applies (13-14% faster on the
-  // Llama MLP shapes); the ping-pong kernel for K % 256 == 128
-  if (gemm_nvfp4_rx_fits(M, N, K, ac, as, bc, bs))
-    return launch_gemm_nvfp4_rx(M, N, K, ac, as, aa, bc, bs, ba, c, ldc, s);
   if (fast)
     hipLaunchKernelGGL(k_gemm_nvfp4_pp, grid, block, kPpLds, s, M, N, K, ac, as, aa, bc, bs, ba,
                        cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0);
@@ -804,6 +819,12 @@ hipError_t launch_nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int6
   hipLaunchKernelGGL(k_nvfp4_expand, dim3((unsigned)g), dim3(256), 0, s,
                      reinterpret_cast<const uint2*>(codes), scales, nblk, static_cast<uint4*>(out));
   return hipGetLastError();
+}
+
+size_t gemm_nvfp4_scratch_bytes(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                                const uint8_t* as, const uint8_t* bc, const uint8_t* bs) {
+  if (!gemm_nvfp4_rx_fits(M, N, K, ac, as, bc, bs)) return 0;
+  return (size_t)gemm_nvfp4_rx_split(M, N, K, device_cus()) * kRxSplitTileBytes;
 }
 
 }  // namespace bsq

@@ -327,31 +327,39 @@ __device__ __forceinline__ void rx_prologue_tiles(RxRegs& r) {
   }
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(kRxThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                      const uint8_t* a_scales, const float* __restrict__ a_amax,
                      const uint8_t* b_codes, const uint8_t* b_scales,
                      const float* __restrict__ b_amax, uint16_t* __restrict__ c, int64_t ldc,
-                     int tiles_m, int tiles_n, int vec_store) {
+                     int tiles_m, int tiles_n, int vec_store, int tiles_full, int tail,
+                     floatx4* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // SPLIT: block h * tail + j computes tile tiles_full + j over the K half h
+  // and writes FP32 partials; otherwise block b computes tile b.
+  const int half = SPLIT ? (int)blockIdx.x / tail : -1;
+  const int pid = SPLIT ? tiles_full + ((int)blockIdx.x - half * tail) : (int)blockIdx.x;
   int tm, tn;
-  tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_of_block(pid, tiles_m, tiles_n, tm, tn);
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1;
   const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)smem;
   RxSrc s;
-  s.a_codes = a_codes;
-  s.a_scales = a_scales;
-  s.b_codes = b_codes;
-  s.b_scales = b_scales;
+  // a K half starts NU units in (64 code bytes and 8 scale bytes per unit and row)
+  const int NU = SPLIT ? (int)(K / 256) : (int)(K / 128);
+  const uint32_t ku = SPLIT ? (uint32_t)(half * NU) : 0u;
+  s.a_codes = a_codes + ku * 64;
+  s.a_scales = a_scales + ku * 8;
+  s.b_codes = b_codes + ku * 64;
+  s.b_scales = b_scales + ku * 8;
   s.m0 = (uint32_t)tm * 256u;
   s.n0 = (uint32_t)tn * 256u;
   s.last_m = (uint32_t)(M - 1);
   s.last_n = (uint32_t)(N - 1);
   s.code_ld = (uint32_t)(K / 2);
   s.scale_ld = (uint32_t)(K / 16);
-  const int NU = (int)(K / 128);
   RxLane ln;
   {
     const int r16 = lane & 15, g = lane >> 4;
@@ -408,6 +416,18 @@ void k_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
   // and the last MFMAs' results have reached the accumulator registers
   lds_barrier();
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (SPLIT) {
+    // FP32 partial of a split tile, in accumulator order: pair (mi, ni) of
+    // thread t at part[((h * tail + j) * 64 + mi * 8 + ni) * 256 + t]
+    floatx4* P = part + ((size_t)(half * tail + (pid - tiles_full)) * 64) * kRxThreads + t;
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni) P[(mi * 8 + ni) * kRxThreads] = acc[mi][ni];
+    return;
+  }
 
   // epilogue: alpha * acc -> BF16 (RNE), staged per wave through LDS so that
   // global stores are 256-byte row segments.  acc[mi][ni] holds, in lane l,
@@ -444,7 +464,54 @@ void k_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
   }
 }
 
+// Second pass of a split last wave: C = BF16_RNE(alpha * (p0 + p1)) for the
+// split tiles, p0 and p1 the partials of the two K halves (same order for
+// every element, so the result is deterministic).  Block b: tile j = b / 4,
+// accumulator rows mi = 2 (b % 4), 2 (b % 4) + 1 of every wave.
+__global__ __launch_bounds__(kRxThreads)
+void k_gemm_nvfp4_rx_join(int64_t M, int64_t N, const floatx4* __restrict__ part,
+                          const float* __restrict__ a_amax, const float* __restrict__ b_amax,
+                          uint16_t* __restrict__ c, int64_t ldc, int tiles_m, int tiles_n,
+                          int tiles_full, int tail, int vec_store) {
+  const int j = blockIdx.x >> 2, q = blockIdx.x & 3;
+  int tm, tn;
+  tile_of_block(tiles_full + j, tiles_m, tiles_n, tm, tn);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+  const float alpha = nvfp4_s_dec(*a_amax) * nvfp4_s_dec(*b_amax) * 16384.0f;
+  const floatx4* P0 = part + (size_t)j * 64 * kRxThreads + t;
+  const floatx4* P1 = part + (size_t)(tail + j) * 64 * kRxThreads + t;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int mi = 2 * q + h;
+    const int64_t gm = (int64_t)tm * 256 + wm * 128 + mi * 16 + (lane & 15);
+    if (gm >= M) continue;
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) {
+      const floatx4 a = P0[(mi * 8 + ni) * kRxThreads], b = P1[(mi * 8 + ni) * kRxThreads];
+      const floatx4 v = a + b;
+      const int64_t gn = (int64_t)tn * 256 + wn * 128 + ni * 16 + (lane >> 4) * 4;
+      const uint32_t lo = pack_bf16x2(v[0] * alpha, v[1] * alpha), hi = pack_bf16x2(v[2] * alpha, v[3] * alpha);
+      uint16_t* dst = c + gm * ldc + gn;
+      if (vec_store && gn + 3 < N) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+      } else {
+        const uint32_t wv[2] = {lo, hi};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gn + e < N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
 }  // namespace
+
+int gemm_nvfp4_rx_split(int64_t M, int64_t N, int64_t K, int cus) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (cus <= 0 || tiles < cus || K % 512 != 0 || K < 4096) return 0;
+  const int tail = (int)(tiles % cus);
+  return tail <= cus / 2 ? tail : 0;
+}
 
 bool gemm_nvfp4_rx_fits(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                         const uint8_t* bc, const uint8_t* bs) {
@@ -456,14 +523,30 @@ bool gemm_nvfp4_rx_fits(int64_t M, int64_t N, int64_t K, const uint8_t* ac, cons
 hipError_t launch_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                                 const uint8_t* as, const float* aa, const uint8_t* bc,
                                 const uint8_t* bs, const float* ba, void* c, int64_t ldc,
-                                hipStream_t s) {
+                                int tail, void* part, hipStream_t s) {
   const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
+  const int tiles = tiles_m * tiles_n, tiles_full = tiles - tail;
   const bool vec_store = (ldc % 8 == 0) && (reinterpret_cast<uintptr_t>(c) % 16 == 0);
-  if (set_lds_limit(reinterpret_cast<const void*>(&k_gemm_nvfp4_rx), kRxLds) != hipSuccess)
+  if (tail < 0 || tail > tiles || (tail > 0 && (part == nullptr || K % 512 != 0)))
+    return hipErrorInvalidValue;
+  if (set_lds_limit(reinterpret_cast<const void*>(&k_gemm_nvfp4_rx<false>), kRxLds) != hipSuccess ||
+      set_lds_limit(reinterpret_cast<const void*>(&k_gemm_nvfp4_rx<true>), kRxLds) != hipSuccess)
     return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k_gemm_nvfp4_rx, dim3((unsigned)(tiles_m * tiles_n)), dim3(kRxThreads), kRxLds,
-                     s, M, N, K, ac, as, aa, bc, bs, ba, static_cast<uint16_t*>(c), ldc, tiles_m,
-                     tiles_n, vec_store ? 1 : 0);
+  uint16_t* cp = static_cast<uint16_t*>(c);
+  floatx4* pp = static_cast<floatx4*>(part);
+  // the full waves, then the split last wave (two K halves per tile) and the
+  // join of its partials
+  if (tiles_full > 0)
+    hipLaunchKernelGGL(k_gemm_nvfp4_rx<false>, dim3((unsigned)tiles_full), dim3(kRxThreads), kRxLds, s,
+                       M, N, K, ac, as, aa, bc, bs, ba, cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0,
+                       tiles_full, 1, nullptr);
+  if (tail > 0) {
+    hipLaunchKernelGGL(k_gemm_nvfp4_rx<true>, dim3((unsigned)(2 * tail)), dim3(kRxThreads), kRxLds, s,
+                       M, N, K, ac, as, aa, bc, bs, ba, cp, ldc, tiles_m, tiles_n, vec_store ? 1 : 0,
+                       tiles_full, tail, pp);
+    hipLaunchKernelGGL(k_gemm_nvfp4_rx_join, dim3((unsigned)(4 * tail)), dim3(kRxThreads), 0, s, M, N, pp,
+                       aa, ba, cp, ldc, tiles_m, tiles_n, tiles_full, tail, vec_store ? 1 : 0);
+  }
   return hipGetLastError();
 }
 

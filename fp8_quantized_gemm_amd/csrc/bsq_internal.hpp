@@ -65,20 +65,39 @@ hipError_t launch_quant_tile(Fmt fmt, bool sr, bool rht_col, bool two_d, const v
 hipError_t launch_fp8_qt(const void* x, int64_t R, int64_t C, const float* amax,
                          uint8_t* codes_row, uint8_t* codes_col, hipStream_t s);
 
-// NVFP4 GEMM (exact FP16 dequant + FP16 MFMA).
+// Number of compute units of the current device (cached per device).
+int device_cus();
+
+// NVFP4 GEMM (exact FP16 dequant + FP16 MFMA).  scratch: null = workspace of
+// the split last wave (see gemm_nvfp4_rx_split) from the stream-ordered
+// allocator; otherwise a device buffer of scratch_bytes used for it
+// (hipErrorInvalidValue when too small).
 hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                              const float* aa, const uint8_t* bc, const uint8_t* bs,
-                             const float* ba, void* c, int64_t ldc, hipStream_t s);
+                             const float* ba, void* c, int64_t ldc, void* scratch,
+                             size_t scratch_bytes, hipStream_t s);
+// Workspace bytes the NVFP4 GEMM of these operands needs on the current device.
+size_t gemm_nvfp4_scratch_bytes(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                                const uint8_t* as, const uint8_t* bc, const uint8_t* bs);
 
 // The register-expansion NVFP4 GEMM (four waves, codes expanded in registers):
 // whether it takes these operands (K % 256 == 0, codes 16-byte and scales
 // 4-byte aligned, each operand below 4 GiB), and its launch.
 bool gemm_nvfp4_rx_fits(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                         const uint8_t* bc, const uint8_t* bs);
+// Split last wave: when the tiles fill at least one wave of `cus` workgroups
+// and leave a last wave of at most cus / 2 tiles (K % 512 == 0, K >= 4096),
+// the number of those tiles; each runs as two workgroups over the two K
+// halves, which write FP32 partials (kRxSplitTileBytes per tile) that a
+// second kernel adds, scales and rounds.  0 = no split.
+int gemm_nvfp4_rx_split(int64_t M, int64_t N, int64_t K, int cus);
+constexpr size_t kRxSplitTileBytes = (size_t)2 * 256 * 256 * 4;
+// tail: gemm_nvfp4_rx_split's count (or 0); part: tail * kRxSplitTileBytes
+// bytes of device memory when tail > 0.
 hipError_t launch_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                                 const uint8_t* as, const float* aa, const uint8_t* bc,
                                 const uint8_t* bs, const float* ba, void* c, int64_t ldc,
-                                hipStream_t s);
+                                int tail, void* part, hipStream_t s);
 
 // NVFP4 GEMM with B pre-expanded to FP16 (bx [N, K] = v * S * 2^-7, from
 // launch_nvfp4_expand).  hipErrorNotSupported unless K % 128 == 0, the
@@ -90,10 +109,11 @@ hipError_t launch_gemm_nvfp4_bx(int64_t M, int64_t N, int64_t K, const uint8_t* 
 hipError_t launch_nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t K,
                                void* out, hipStream_t s);
 
-// C[M, N] = alpha * A . B^T, block-scaled operands, BF16 out.
+// C[M, N] = alpha * A . B^T, block-scaled operands, BF16 out.  scratch as
+// for launch_gemm_nvfp4 (only NVFP4 uses it).
 hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,
-                       hipStream_t s);
+                       void* scratch, size_t scratch_bytes, hipStream_t s);
 
 }  // namespace bsq

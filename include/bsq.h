@@ -268,6 +268,14 @@ bsq_status fp8_quantize_transpose(const void* x, int64_t rows, int64_t cols, uin
  *          b_amax required; alpha = s_dec(a_amax) * s_dec(b_amax) with
  *          s_dec = 1/(448/amax).  Requires K % 32 == 0.
  * M and N may be any value >= 0.  C must not alias any input.
+ * Workspace (NVFP4 only): when the 256 x 256 output tiles fill at least one
+ * wave of the device's compute units and leave a last wave of at most half
+ * of them (K % 512 == 0, K >= 4096), each tile of that last wave is computed
+ * as two FP32 partial sums over the two halves of K, added in a second
+ * kernel (the same order for every element: repeated calls give identical
+ * bits; the sum differs from a one-pass accumulation only in FP32 rounding).
+ * Their 512 KiB per tile come from the stream-ordered allocator
+ * (hipMallocAsync / hipFreeAsync on `stream`); BSQ_EHIP if that fails.
  */
 bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K,
                    const uint8_t* a_codes, const uint8_t* a_scales, const float* a_amax,
@@ -292,7 +300,8 @@ bsq_status nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t row
  * DGRAD, WGRAD consume NVFP4 operands, emit BF16) with B handed over as its
  * FP16 expansion (nvfp4_expand of B's codes and scales): the kernel expands
  * only A.  The result is bit-identical to bs_gemm(BSQ_NVFP4, ...) on the
- * same operands.  For operands used by several GEMMs or much smaller than
+ * same operands whenever bs_gemm does not split its last wave over K (see
+ * bs_gemm's workspace note).  For operands used by several GEMMs or much smaller than
  * the other operand (weights, the smaller WGRAD input), expanding once and
  * streaming FP16 costs less than expanding inside every output tile.
  *   a_codes [M, K/2], a_scales [M, K/16], a_amax : the NVFP4 A operand.

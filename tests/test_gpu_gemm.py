@@ -138,6 +138,30 @@ def test_mx_square_4096(fmt):
     assert rep["frac_equal_rne"] > 0.95
 
 
+def test_nvfp4_split_last_wave():
+    """A GEMM whose last wave of 256 x 256 tiles would leave most compute
+    units idle: 16 tile rows and one tile column more than a wave, so the
+    last wave holds 16 tiles, each computed as two K halves and joined
+    (ragged M and N: the edge tiles are among them).  Whole output against
+    the oracle, and a second launch must give the same bits."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles_n = cus // 16 + 1
+    M, N, K = 16 * 256 - 24, tiles_n * 256 - 40, 4096
+    announce("nvfp4 split last wave", M, N, K, "cus", cus)
+    A = synth.bf16_tensor((M, K), 4100, device="cuda")
+    B = synth.bf16_tensor((N, K), 4101, sigma=0.02, outliers=False, device="cuda")
+    ac, as_, aa = bsq.nvfp4_quantize(A, 1)
+    bc, bs, ba = bsq.nvfp4_quantize(B, 1)
+    C = bsq.bs_gemm("nvfp4", ac, as_, bc, bs, aa, ba)
+    C2 = bsq.bs_gemm("nvfp4", ac, as_, bc, bs, aa, ba)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "second launch differs"
+    oac, oas, oaa = Q.nvfp4_quantize(bits(A), 1)
+    obc, obs, oba = Q.nvfp4_quantize(bits(B), 1)
+    rep = _check(C, G.gemm_nvfp4(oac, oas, oaa, obc, obs, oba), f"nvfp4 split {M}x{N}x{K}")
+    assert rep["frac_equal_rne"] > 0.95
+
+
 def test_ldc_and_k_zero():
     announce("ldc / K=0")
     A = synth.bf16_tensor((64, 64), 5, device="cuda")
