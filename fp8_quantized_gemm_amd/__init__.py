@@ -21,8 +21,8 @@ FORMATS = {"nvfp4": 0, "mxfp4": 1, "mxfp8": 2, "fp8": 3}
 ROUNDING = {"rne": 0, "sr": 1}
 ABI_SYMBOLS = ("nvfp4_quantize", "mx_quantize", "quantize_transpose", "quantize_transpose_amax",
                "fp8_quantize_transpose", "swiglu_amax", "swiglu_backward_amax",
-               "master_weight_update", "nvfp4_expand", "bs_gemm", "bs_gemm_nvfp4_bx",
-               "bsq_status_string")
+               "master_weight_update", "nvfp4_expand", "bs_gemm", "bs_gemm_noalloc",
+               "bs_gemm_nvfp4_bx", "bsq_status_string")
 
 
 class BsqError(RuntimeError):
@@ -55,6 +55,7 @@ def lib():
         L.swiglu_backward_amax.argtypes = [P, P, I64, I64, I, U16, P, P, P, P]
         L.master_weight_update.argtypes = [P, P, I64, ctypes.c_float, P, P, P]
         L.bs_gemm.argtypes = [I, I64, I64, I64, P, P, P, P, P, P, P, I64, P]
+        L.bs_gemm_noalloc.argtypes = [I, I64, I64, I64, P, P, P, P, P, P, P, I64, P]
         L.nvfp4_expand.argtypes = [P, P, I64, I64, P, P]
         L.bs_gemm_nvfp4_bx.argtypes = [I64, I64, I64, P, P, P, P, P, P, I64, P]
         for fn in ABI_SYMBOLS[:-1]:
@@ -333,6 +334,31 @@ def bs_gemm(fmt, a_codes, a_scales, b_codes, b_scales, a_amax=None, b_amax=None,
     st = lib().bs_gemm(FORMATS[fmt], M, N, int(K), _ptr(a_codes), _ptr(a_scales), _ptr(a_amax),
                        _ptr(b_codes), _ptr(b_scales), _ptr(b_amax), _ptr(out), ldc, _stream(dev))
     _check("bs_gemm", st)
+    return out
+
+
+def bs_gemm_noalloc(fmt, a_codes, a_scales, b_codes, b_scales, a_amax, b_amax, out, K=None):
+    """bs_gemm into a caller-provided `out`, through the entry point that
+    allocates no device memory (its NVFP4 workspace is the library's static
+    per-device array; overlapping calls on one device race)."""
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt!r}")
+    if K is None and isinstance(a_codes, torch.Tensor) and a_codes.dim() == 2:
+        K = a_codes.shape[1] * (1 if fmt in ("mxfp8", "fp8") else 2)
+    K = int(K)
+    _check_operand("A", a_codes, a_scales, K, fmt)
+    _check_operand("B", b_codes, b_scales, K, fmt)
+    if fmt in ("nvfp4", "fp8") and (a_amax is None or b_amax is None):
+        raise ValueError(f"{fmt} needs both per-tensor amaxes")
+    _check_amax(a_amax, b_amax)
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    _check_out(out, M, N, torch.bfloat16)
+    _check_device(a_codes, a_scales, b_codes, b_scales, a_amax, b_amax, out=out)
+    ldc = out.stride(0) if out.dim() == 2 else N
+    st = lib().bs_gemm_noalloc(FORMATS[fmt], M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(a_amax),
+                               _ptr(b_codes), _ptr(b_scales), _ptr(b_amax), _ptr(out), ldc,
+                               _stream(out.device))
+    _check("bs_gemm_noalloc", st)
     return out
 
 

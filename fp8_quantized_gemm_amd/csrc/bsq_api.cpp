@@ -28,17 +28,16 @@ hipError_t set_lds_limit(const void* fn, int bytes) {
 }
 
 int device_cus() {
+  constexpr int kMaxDevices = 64;
   static std::mutex mu;
-  static std::map<int, int> cus;   // device -> compute units
+  static int cus[kMaxDevices] = {};   // device -> compute units (0: not looked up yet)
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   std::lock_guard<std::mutex> lock(mu);
-  const auto it = cus.find(dev);
-  if (it != cus.end()) return it->second;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-  cus.emplace(dev, n);
-  return n;
+  if (cus[dev] == 0 &&
+      hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus[dev] = 0;
+  return cus[dev];
 }
 
 }  // namespace bsq
@@ -61,6 +60,42 @@ bool too_many(int64_t a, int64_t b) { return a > 0 && b > (((int64_t)1 << 48) / 
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
   return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+// Checks and dispatch of bs_gemm (static_scratch false: the NVFP4 split
+// workspace from the stream-ordered allocator) and bs_gemm_noalloc (true:
+// the library's static per-device workspace, nothing allocated).
+bsq_status gemm_common(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                       const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
+                       const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,
+                       void* stream, bool static_scratch) {
+  if (fmt != BSQ_NVFP4 && fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8 && fmt != BSQ_FP8) return BSQ_EINVAL;
+  const bool per_tensor = fmt == BSQ_NVFP4 || fmt == BSQ_FP8;   // alpha from the two amaxes
+  if (M < 0 || N < 0 || K < 0) return BSQ_EINVAL;
+  if (K % (fmt == BSQ_NVFP4 ? 16 : 32) != 0) return BSQ_EINVAL;
+  if (ldc < N || ldc < 0) return BSQ_EINVAL;
+  if (too_many(M, K) || too_many(N, K) || too_many(M, ldc)) return BSQ_EINVAL;
+  if (M > (int64_t)256 * 0x7FFFFF || N > (int64_t)256 * 0x7FFFFF) return BSQ_EINVAL;
+  if (M == 0 || N == 0) return BSQ_OK;
+  if (!c || ((reinterpret_cast<uintptr_t>(c) & 1u) != 0)) return BSQ_EINVAL;
+  if (K > 0) {
+    if (!a_codes || !b_codes) return BSQ_EINVAL;
+    if (fmt != BSQ_FP8 && (!a_scales || !b_scales)) return BSQ_EINVAL;
+  }
+  if (per_tensor && (!a_amax || !b_amax)) return BSQ_EINVAL;
+  const bsq::Fmt f = fmt == BSQ_NVFP4 ? bsq::kNVFP4
+                     : fmt == BSQ_MXFP4 ? bsq::kMXFP4
+                     : fmt == BSQ_MXFP8 ? bsq::kMXFP8 : bsq::kFP8;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (static_scratch && fmt == BSQ_NVFP4) {
+    if (bsq::gemm_nvfp4_static_scratch(&scratch, &scratch_bytes) != hipSuccess) return BSQ_EHIP;
+    if (bsq::gemm_nvfp4_scratch_bytes(M, N, K, a_codes, a_scales, b_codes, b_scales) > scratch_bytes)
+      return BSQ_EUNSUPPORTED;
+  }
+  return hip_status(bsq::launch_gemm(f, M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales,
+                                     b_amax, c, ldc, scratch, scratch_bytes,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 // Shared checks and dispatch of the SwiGLU forward (dh null) and backward.
@@ -321,25 +356,16 @@ bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K, const uint8_
                    const uint8_t* a_scales, const float* a_amax, const uint8_t* b_codes,
                    const uint8_t* b_scales, const float* b_amax, void* c, int64_t ldc,
                    void* stream) {
-  if (fmt != BSQ_NVFP4 && fmt != BSQ_MXFP4 && fmt != BSQ_MXFP8 && fmt != BSQ_FP8) return BSQ_EINVAL;
-  const bool per_tensor = fmt == BSQ_NVFP4 || fmt == BSQ_FP8;   // alpha from the two amaxes
-  if (M < 0 || N < 0 || K < 0) return BSQ_EINVAL;
-  if (K % (fmt == BSQ_NVFP4 ? 16 : 32) != 0) return BSQ_EINVAL;
-  if (ldc < N || ldc < 0) return BSQ_EINVAL;
-  if (too_many(M, K) || too_many(N, K) || too_many(M, ldc)) return BSQ_EINVAL;
-  if (M > (int64_t)256 * 0x7FFFFF || N > (int64_t)256 * 0x7FFFFF) return BSQ_EINVAL;
-  if (M == 0 || N == 0) return BSQ_OK;
-  if (!c || ((reinterpret_cast<uintptr_t>(c) & 1u) != 0)) return BSQ_EINVAL;
-  if (K > 0) {
-    if (!a_codes || !b_codes) return BSQ_EINVAL;
-    if (fmt != BSQ_FP8 && (!a_scales || !b_scales)) return BSQ_EINVAL;
-  }
-  if (per_tensor && (!a_amax || !b_amax)) return BSQ_EINVAL;
-  const bsq::Fmt f = fmt == BSQ_NVFP4 ? bsq::kNVFP4
-                     : fmt == BSQ_MXFP4 ? bsq::kMXFP4
-                     : fmt == BSQ_MXFP8 ? bsq::kMXFP8 : bsq::kFP8;
-  return hip_status(bsq::launch_gemm(f, M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales,
-                                     b_amax, c, ldc, nullptr, 0, static_cast<hipStream_t>(stream)));
+  return gemm_common(fmt, M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax, c, ldc,
+                     stream, false);
+}
+
+bsq_status bs_gemm_noalloc(bsq_format fmt, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_amax,
+                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_amax,
+                           void* c, int64_t ldc, void* stream) {
+  return gemm_common(fmt, M, N, K, a_codes, a_scales, a_amax, b_codes, b_scales, b_amax, c, ldc,
+                     stream, true);
 }
 
 }  // extern "C"

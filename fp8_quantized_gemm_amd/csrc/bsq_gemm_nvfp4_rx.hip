@@ -55,6 +55,8 @@
 #include "bsq_gemm_common.hpp"
 #include "bsq_internal.hpp"
 
+#include <mutex>
+
 namespace bsq {
 
 namespace {
@@ -505,6 +507,35 @@ void k_gemm_nvfp4_rx_join(int64_t M, int64_t N, const floatx4* __restrict__ part
 }
 
 }  // namespace
+
+// Workspace of the split last wave for callers that cannot allocate
+// (bs_gemm_noalloc): FP32 partials of at most 128 split tiles, which is what
+// the split needs on 256 compute units.  Each device that loads this code
+// holds its own copy until the process ends; host code uses the address
+// that hipGetSymbolAddress returns for the current device, never the name.
+constexpr size_t kRxScratchBytes = (size_t)128 * kRxSplitTileBytes;   // 64 MiB
+static __device__ __align__(256) uint8_t scratch[kRxScratchBytes];
+
+hipError_t gemm_nvfp4_static_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kRxScratchBytes;
+  return hipSuccess;
+}
 
 int gemm_nvfp4_rx_split(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);

@@ -76,6 +76,9 @@ hipError_t launch_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                              const float* aa, const uint8_t* bc, const uint8_t* bs,
                              const float* ba, void* c, int64_t ldc, void* scratch,
                              size_t scratch_bytes, hipStream_t s);
+// The library's static workspace for the NVFP4 GEMM on the current device
+// (address looked up once per device) and its size.
+hipError_t gemm_nvfp4_static_scratch(void** ptr, size_t* bytes);
 // Workspace bytes the NVFP4 GEMM of these operands needs on the current device.
 size_t gemm_nvfp4_scratch_bytes(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                                 const uint8_t* as, const uint8_t* bc, const uint8_t* bs);

@@ -283,6 +283,23 @@ bsq_status bs_gemm(bsq_format fmt, int64_t M, int64_t N, int64_t K,
                    void* c, int64_t ldc, void* stream);
 
 /*
+ * bs_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks and results (bit for bit) as bs_gemm; the NVFP4
+ * split-last-wave workspace is the library's static per-device array of
+ * 64 MiB (held by each device the library runs on until the process ends)
+ * instead of the stream-ordered allocator, and no call allocates.  The
+ * first call on a device looks up that array's address (make it outside
+ * graph capture).  Returns BSQ_EUNSUPPORTED if the split would need more
+ * than 64 MiB (more than 256 compute units).  Calls that overlap on one
+ * device (other streams, other host threads) share the array and race.
+ */
+bsq_status bs_gemm_noalloc(bsq_format fmt, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_amax,
+                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_amax,
+                           void* c, int64_t ldc, void* stream);
+
+/*
  * FP16 expansion of an NVFP4 operand (recipe ingredients 1-2: E2M1 codes
  * under E4M3 block scales), without its per-tensor scale:
  *   out[r, k] = v * S * 2^-7   (FP16, exact: v * S has at most 6 significant

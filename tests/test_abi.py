@@ -197,9 +197,11 @@ def test_expand_and_gemm_bx_argument_errors():
     assert g(M=0) == bsq.BSQ_OK
 
 
-def test_bs_gemm_argument_errors():
+@pytest.mark.parametrize("entry", ["bs_gemm", "bs_gemm_noalloc"])
+def test_bs_gemm_argument_errors(entry):
     L = bsq.lib()
-    g = lambda fmt=0, M=16, N=16, K=32, ldc=16, a=FAKE, amax=FAKE, c=FAKE: L.bs_gemm(
+    fn = getattr(L, entry)
+    g = lambda fmt=0, M=16, N=16, K=32, ldc=16, a=FAKE, amax=FAKE, c=FAKE: fn(
         fmt, M, N, K, a, FAKE, amax, FAKE, FAKE, amax, c, ldc, None)
     assert g(K=24) == bsq.BSQ_EINVAL                      # NVFP4 K % 16
     assert g(fmt=1, K=48) == bsq.BSQ_EINVAL               # MX K % 32
@@ -210,11 +212,11 @@ def test_bs_gemm_argument_errors():
     assert g(fmt=9) == bsq.BSQ_EINVAL
     assert g(M=0) == bsq.BSQ_OK and g(N=0) == bsq.BSQ_OK  # empty output: nothing to launch
     # per-tensor FP8: scales may be NULL, both amaxes are required
-    f = lambda K=64, amax=FAKE, sc=None: L.bs_gemm(3, 16, 16, K, FAKE, sc, amax, FAKE, sc, amax,
-                                                     FAKE, 16, None)
+    f = lambda K=64, amax=FAKE, sc=None: fn(3, 16, 16, K, FAKE, sc, amax, FAKE, sc, amax,
+                                            FAKE, 16, None)
     assert f(K=48) == bsq.BSQ_EINVAL                      # K % 32
     assert f(amax=None) == bsq.BSQ_EINVAL
-    assert L.bs_gemm(1, 16, 16, 64, FAKE, None, None, FAKE, None, None, FAKE, 16, None) == bsq.BSQ_EINVAL
+    assert fn(1, 16, 16, 64, FAKE, None, None, FAKE, None, None, FAKE, 16, None) == bsq.BSQ_EINVAL
 
 
 def test_ceiling_library_loads_and_checks_arguments():
