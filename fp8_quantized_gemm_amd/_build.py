@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libbsq.so")
 CEILING_LIB = os.path.join(PKG, "libbsq_ceiling.so")
 
 SOURCES = ["bsq_api.cpp", "bsq_quantize.hip", "bsq_gemm.hip", "bsq_gemm_nvfp4.hip",
-           "bsq_gemm_nvfp4_rx.hip"]
+           "bsq_gemm_nvfp4_rx.hip", "bsq_gemm_mx_rx.hip"]
 CEILING_SOURCES = ["route_a_ceiling.hip"]
 
 ARCH = "gfx950"

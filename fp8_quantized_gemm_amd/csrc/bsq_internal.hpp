@@ -112,6 +112,17 @@ hipError_t launch_gemm_nvfp4_bx(int64_t M, int64_t N, int64_t K, const uint8_t* 
 hipError_t launch_nvfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t K,
                                void* out, hipStream_t s);
 
+// The four-wave MX / per-tensor FP8 GEMM (FMT kMXFP4, kMXFP8, kFP8): whether it
+// takes these operands (K % 512 == 0, codes and scales 16-byte aligned, 32-bit
+// offsets suffice), and its launch.
+template <int FMT>
+bool gemm_mx_rx_fits(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                     const uint8_t* bc, const uint8_t* bs);
+template <int FMT>
+hipError_t launch_gemm_mx_rx(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                             const float* aa, const uint8_t* bc, const uint8_t* bs, const float* ba,
+                             void* c, int64_t ldc, hipStream_t s);
+
 // C[M, N] = alpha * A . B^T, block-scaled operands, BF16 out.  scratch as
 // for launch_gemm_nvfp4 (only NVFP4 uses it).
 hipError_t launch_gemm(Fmt fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,

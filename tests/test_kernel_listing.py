@@ -1,6 +1,7 @@
-"""Static checks of the register-expansion NVFP4 GEMM's gfx950 assembly.
+"""Static checks of the gfx950 assembly of the GEMMs whose MFMAs are inline
+assembly: the register-expansion NVFP4 GEMM and the four-wave MX GEMM.
 
-Its MFMAs are inline assembly (so that every accumulator tile keeps fixed
+Their MFMAs are inline assembly (so that every accumulator tile keeps fixed
 registers), and the compiler's hazard recognizer does not see their operand
 timing.  The kernel's correctness then rests on the code the compiler emits
 around them, which these checks read from a fresh `hipcc -S` of the source:
@@ -157,19 +158,28 @@ def test_checker_flags_fragment_written_just_before_mfma():
 
 # ------------------------------------------------------------------ the kernel
 
-@pytest.fixture(scope="module")
-def rx_asm():
+def _compile(src):
     hipcc = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
     from fp8_quantized_gemm_amd import _build
     with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "rx.s")
-        cmd = [hipcc] + _build.FLAGS + ["-x", "hip", "--cuda-device-only", "-S",
-                                        os.path.join(CSRC, "bsq_gemm_nvfp4_rx.hip"), "-o", out]
+        out = os.path.join(d, "k.s")
+        cmd = [hipcc] + _build.FLAGS + ["-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src),
+                                        "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         return open(out).read()
+
+
+@pytest.fixture(scope="module")
+def rx_asm():
+    return _compile("bsq_gemm_nvfp4_rx.hip")
+
+
+@pytest.fixture(scope="module")
+def mx_asm():
+    return _compile("bsq_gemm_mx_rx.hip")
 
 
 def test_rx_kernels_present(rx_asm):
@@ -180,13 +190,22 @@ def test_rx_kernels_present(rx_asm):
         assert len(_instructions(body)) > 0
 
 
-def test_rx_mfma_operand_timing(rx_asm):
-    funcs = _functions(rx_asm, "k_gemm_nvfp4_rx")
+def _check_kernels(funcs, skip=()):
     report = []
     for name, body in funcs.items():
-        if "join" in name:
+        if any(k in name for k in skip):
             continue
         n_mfma = sum(1 for mn, _ in _instructions(body) if mn.startswith("v_mfma"))
         assert n_mfma > 0, name
         report += [f"{name}: {t}" for _, t in hazards(body)]
     assert report == [], "\n".join(report[:20])
+
+
+def test_rx_mfma_operand_timing(rx_asm):
+    _check_kernels(_functions(rx_asm, "k_gemm_nvfp4_rx"), skip=("join",))
+
+
+def test_mx_mfma_operand_timing(mx_asm):
+    funcs = _functions(mx_asm, "k_gemm_mx_rx")
+    assert len(funcs) == 3, list(funcs)                       # MXFP4, MXFP8, per-tensor FP8
+    _check_kernels(funcs)
