@@ -571,7 +571,7 @@ def mx_square(device, reps=20):
 
 
 def gemm_traffic(workload):
-    """HBM bytes per k_gemm_nvfp4 launch from the committed rocprofv3 FETCH_SIZE /
+    """HBM bytes per NVFP4 GEMM call (all its dispatches) from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary of this workload, or None when the kernel sources have
     changed since those counters were taken (the summary stores their SHA-256)."""
     import hashlib
@@ -771,12 +771,13 @@ def main():
                    "pct_of_fp16_mfma_peak": round(100 * value / PEAK_FP16_TFLOPS, 2)},
         "timing": (f"median of {args.steps} steps (HIP events on the launch stream), a 1 GiB "
                    f"scratch read between steps; mean {sum(ms_list) / len(ms_list):.4f} ms"),
-        "roofline": {"bound": "mfma", "kernel": ("NVFP4 GEMM, 6 launches per step: k_gemm_nvfp4_rx" +
+        "roofline": {"bound": "mfma", "kernel": ("NVFP4 GEMM, 6 calls per step: k_gemm_nvfp4_rx (a last wave of "
+                                                 "tiles filling at most half the CUs split over K + join)" +
                                                  "".join(f"; k_gemm_nvfp4_px for {n}" for n, v in step.bx.items() if v)),
                      "achieved": round(gemm_tflops, 1), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": gemm_traffic(args.workload),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)"},
+                     "traffic_unit": "HBM bytes per GEMM call (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)"},
         "breakdown": breakdown,
         ("rht_off" if not args.no_rht else "rht_on"): {
             "ms_per_step": round(ms_other, 4),
