@@ -162,6 +162,42 @@ def test_nvfp4_split_last_wave():
     assert rep["frac_equal_rne"] > 0.95
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp8"])
+def test_multi_wave_odd_row_stride(fmt):
+    """More tiles than one wave, written into a column slice of a wider
+    tensor (row stride N + 3, so every epilogue takes its element-wise store
+    path): NVFP4 with a split last wave (its join too), MX on the four-wave
+    kernel.  Whole output against the oracle; the three padding columns keep
+    their value."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if fmt == "nvfp4":
+        M, N, K = 16 * 256 - 24, (cus // 16 + 1) * 256 - 40, 4096
+    else:
+        M, N, K = 17 * 256 - 8, 17 * 256 - 24, 1024
+    announce("multi-wave odd ldc", fmt, M, N, K)
+    A = synth.bf16_tensor((M, K), 4200 + M, device="cuda")
+    B = synth.bf16_tensor((N, K), 4300 + N, sigma=0.02, outliers=False, device="cuda")
+    wide = torch.full((M, N + 3), 5.0, dtype=torch.bfloat16, device="cuda")
+    out = wide[:, :N]
+    if fmt == "nvfp4":
+        ac, as_, aa = bsq.nvfp4_quantize(A, 1)
+        bc, bs, ba = bsq.nvfp4_quantize(B, 1)
+        bsq.bs_gemm("nvfp4", ac, as_, bc, bs, aa, ba, out=out)
+        oac, oas, oaa = Q.nvfp4_quantize(bits(A), 1)
+        obc, obs, oba = Q.nvfp4_quantize(bits(B), 1)
+        ref = G.gemm_nvfp4(oac, oas, oaa, obc, obs, oba)
+    else:
+        ac, as_ = bsq.mx_quantize(A, fmt)
+        bc, bs = bsq.mx_quantize(B, fmt)
+        bsq.bs_gemm(fmt, ac, as_, bc, bs, K=K, out=out)
+        oac, oas = Q.mx_quantize(bits(A), fmt)
+        obc, obs = Q.mx_quantize(bits(B), fmt)
+        ref = G.gemm_mx(oac, oas, obc, obs, fmt)
+    torch.cuda.synchronize()
+    assert bool((wide[:, N:] == 5.0).all()), "padding columns written"
+    _check(out, ref, f"{fmt} {M}x{N}x{K} ldc {N + 3}")
+
+
 def test_ldc_and_k_zero():
     announce("ldc / K=0")
     A = synth.bf16_tensor((64, 64), 5, device="cuda")
