@@ -24,6 +24,10 @@ Also reported, each in its own field:
                          FP8 matrix path) and the NVFP4 step's speed relative
                          to it, also against the vendor's FP8 GEMM
                          (hipBLASLt via torch._scaled_mm) on the same codes;
+  vendor_fp16_gemm       for scale: the vendor's FP16 GEMM (hipBLASLt via
+                         torch.mm) on the six GEMMs with both operands
+                         pre-expanded to the FP16 values the NVFP4 GEMM forms
+                         in its tiles (expansion not timed);
   workload_405b          the Llama-3.1-405B MLP layer step (8,192 tokens,
                          hidden 16384, FFN 53248), same method;
   tiny_fprop_256         the 256^3 NVFP4 FPROP (quantize + GEMM);
@@ -37,7 +41,7 @@ Also reported, each in its own field:
   nvfp4_route_ceilings   inner-loop ceilings of the two exact NVFP4 GEMM routes.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--no-rht]
-[--workload 8b|405b] [--no-cpu-baseline] [--no-mx] [--no-fp8] [--no-swiglu]
+[--workload 8b|405b] [--no-cpu-baseline] [--no-mx] [--no-fp8] [--no-vendor-fp16] [--no-swiglu]
 [--no-route-ceiling] [--no-405b] [--no-tiny] [--no-bx].
 """
 
@@ -361,6 +365,36 @@ def fp8_baseline(step, steps, warmup, nvfp4_ms, flush):
     f.vendor = False
     del f
     return out
+
+
+def vendor_fp16_gemm(step, nvfp4_gemm_ms, flush, reps=5):
+    """For scale: the vendor's FP16 GEMM (hipBLASLt through torch.mm) on the
+    step's six GEMMs with both operands pre-expanded to the same FP16 values
+    the NVFP4 GEMM forms in its tiles (nvfp4_expand of the step's codes and
+    scales), FP32 accumulation.  Pure GEMM time, flushed medians; the
+    expansion is not timed.  One GEMM's operands are held at a time."""
+    tot = 0.0
+    per = {}
+    for name, (an, ao), (bn, bo), M, N, K in step.gemms:
+        a, b = step.q[an], step.q[bn]
+        A16 = bsq.nvfp4_expand(a[ao + "c"], a[ao + "s"])
+        B16 = bsq.nvfp4_expand(b[bo + "c"], b[bo + "s"])
+        C16 = torch.empty((M, N), dtype=torch.float16, device=step.dev)
+        run = lambda ev: torch.mm(A16, B16.t(), out=C16)
+        for _ in range(2):
+            run(None)
+        ms_list, _ = timed_reps(run, reps, flush)
+        per[name] = median(ms_list)
+        tot += per[name]
+        del A16, B16, C16
+        torch.cuda.empty_cache()
+    tf = step.flops / (tot * 1e-3) / 1e12
+    return {"gemm": "hipBLASLt FP16 GEMM (torch.mm) on both operands pre-expanded to FP16 (nvfp4_expand), "
+                    "the values the NVFP4 GEMM forms in its tiles; expansion not timed",
+            "gemm_ms": round(tot, 4), "gemm_tflops": round(tf, 1),
+            "gemm_frac_of_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4),
+            "per_gemm_tflops": {k: round(step.gemm_flops[k] / (v * 1e-3) / 1e12, 1) for k, v in per.items()},
+            "nvfp4_gemm_over_vendor_fp16": round(tot / nvfp4_gemm_ms, 4)}
 
 
 def swiglu_fused(step, reps=10):
@@ -711,6 +745,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MX square-GEMM lines")
     ap.add_argument("--no-fp8", action="store_true", help="skip the per-tensor FP8 baseline step")
+    ap.add_argument("--no-vendor-fp16", action="store_true",
+                    help="skip the vendor FP16 GEMM on pre-expanded operands (for scale)")
     ap.add_argument("--no-swiglu", action="store_true", help="skip the fused SwiGLU + quantize lines")
     ap.add_argument("--no-bx", action="store_true",
                     help="expand every B operand inside the GEMM (no pre-expanded weights)")
@@ -786,6 +822,8 @@ def main():
     }
     if not args.no_fp8:
         out["fp8_baseline"] = fp8_baseline(step, args.steps, args.warmup, ms, flush)
+    if not args.no_vendor_fp16:
+        out["vendor_fp16_gemm"] = vendor_fp16_gemm(step, step.flops / (gemm_tflops * 1e12) * 1e3, flush)
     if not args.no_swiglu:
         out["swiglu_fused_quantize"] = swiglu_fused(step)
         out["mlp_layer_step"] = mlp_layer_step(step, args.steps, args.warmup)
