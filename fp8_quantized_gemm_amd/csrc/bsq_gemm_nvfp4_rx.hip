@@ -30,13 +30,16 @@
 // rounding).
 //
 // Pipeline per unit U (four steps of 64 MFMAs):
-//  * raw units reach LDS by global -> LDS direct loads (per row 64 code bytes
-//    as four 16-byte chunks, and 8 scale bytes), four unit buffers, units
-//    issued three ahead; wave w loads A rows and B rows 64 w .. 64 w + 63,
-//    its 12 loads spread over the unit's 256 MFMAs (one every 21) rather
-//    than issued in one burst; one workgroup barrier per unit makes a
-//    landed unit visible to all waves and retires the buffer the unit three
-//    ahead will fill;
+//  * raw units reach LDS by global -> LDS direct loads in pairs (units 2 p,
+//    2 p + 1): per row 128 code bytes as eight 16-byte chunks, so the eight
+//    lanes of a row read one whole 128-byte line (64-byte pieces cost as many
+//    L2 requests as whole lines and halved the rate the tiles draw from the
+//    L2), and 16 scale bytes; two pair buffers; wave w loads A rows and B
+//    rows 64 w .. 64 w + 63; an odd unit U issues pair (U + 3) / 2, its 18
+//    loads spread over the unit's 256 MFMAs (one every 14), into the buffer
+//    of units U - 1 and U, whose codes and scales were read during the unit
+//    before each; one workgroup barrier per unit makes a landed unit visible
+//    to all waves;
 //  * each tile's 16 code bytes for the unit (its four steps) are read from
 //    LDS in one piece, as soon as the previous unit's last expansion from
 //    them is done, about a step ahead of their first use; the scales of
@@ -48,10 +51,10 @@
 // inline assembly, so the compiler's hazard recognizer does not see those
 // dependencies: every fragment is complete at least one MFMA before its first
 // reader, and explicit s_nop cover the register copies at step boundaries.
-// LDS code rows are 64 bytes: the 16-byte chunk c of row r sits at slot
-// c ^ swz(r), swz(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1).  A 16-byte read is
-// served eight lanes at a time by 32 four-byte banks; the eight lanes (eight
-// consecutive rows, one lane group) then touch 32 distinct banks.
+// LDS code rows are 128 bytes (a pair): the 16-byte chunk c of row r sits at
+// slot c ^ swz(r), swz(r) = (r >> 1) & 7.  A 16-byte read is served sixteen
+// lanes (sixteen consecutive rows, one chunk) per cycle by 64 four-byte banks;
+// rows of one parity start on the same bank, so their eight slots must differ.
 #include "bsq_gemm_common.hpp"
 #include "bsq_internal.hpp"
 
@@ -64,18 +67,25 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRxThreads = 256;
-constexpr int kRxCodeB = 256 * 64;                      // one operand's codes of a 128-K unit
-constexpr int kRxOpB = kRxCodeB + 256 * 8;              // plus its scales: 18 KiB
-constexpr int kRxUnitB = 2 * kRxOpB;                    // A then B: 36 KiB
-constexpr int kRxNBuf = 4;                              // raw unit buffers
+// Units of 128 K (64 code bytes and 8 scale bytes per row) are staged in
+// pairs: a pair buffer holds two consecutive units, each row's 128 code bytes
+// and 16 scale bytes contiguous, so that every direct load reads whole
+// 128-byte lines (code) or whole 16-byte scale pieces.
+constexpr int kRxRowB = 128;                            // code bytes per row and pair
+constexpr int kRxCodeB = 256 * kRxRowB;                 // one operand's codes of a pair: 32 KiB
+constexpr int kRxOpB = kRxCodeB + 256 * 16;             // plus its scales: 36 KiB
+constexpr int kRxUnitB = 2 * kRxOpB;                    // A then B: one pair buffer, 72 KiB
+constexpr int kRxNBuf = 2;                              // pair buffers
 constexpr int kRxLds = kRxNBuf * kRxUnitB;              // 147456
 constexpr int kRxEpiRowB = 272;                         // epilogue: 128 BF16 + 16 bytes pad per row
-constexpr int kRxLoadsPerUnit = 12;                     // direct loads per wave and unit
-static_assert(2 * kRxLoadsPerUnit <= 63, "the wait counts of two units fit the load counter");
+constexpr int kRxLoadsPerPair = 18;                     // direct loads per wave and pair
+static_assert(2 * kRxLoadsPerPair <= 63, "the wait counts of two pairs fit the load counter");
 static_assert(4 * 128 * kRxEpiRowB <= kRxLds, "epilogue staging must fit");
 static_assert(kRxLds <= 160 * 1024, "LDS plan");
 
-__host__ __device__ constexpr int rx_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// a 16-byte read is served 16 lanes (16 consecutive rows, one chunk) per
+// cycle across 64 banks: the 128-byte rows of one parity take distinct slots
+__host__ __device__ constexpr int rx_swz(int r) { return (r >> 1) & 7; }
 
 // Where the operands come from (all wave-uniform).
 struct RxSrc {
@@ -87,53 +97,52 @@ struct RxSrc {
   uint32_t code_ld, scale_ld;          // bytes per operand row
 };
 
-// Direct loads of raw unit `u` (K elements 128 u .. 128 u + 127) of A rows and
-// B rows 64 w .. 64 w + 63 of the tile into the unit buffer at LDS address
-// `raw`, load Q (0..11) of 12: Q / 6 picks the operand; Q % 6 < 4 is a code
-// load of 16 rows x 64 bytes, one 16-byte chunk per lane (lane l fills row
-// l >> 2, slot l & 3 of the 16 rows with the chunk that belongs there);
-// 4-5 a scale load of 32 rows x 8 bytes.  Rows past the operand re-read its
-// last row (their results are never stored).  32-bit offsets: operands are
-// below 4 GiB.
+// Direct loads of pair `p` (units 2 p, 2 p + 1: K elements 256 p .. 256 p + 255)
+// of A rows and B rows 64 w .. 64 w + 63 of the tile into the pair buffer at
+// LDS address `raw`, load Q (0..17) of 18: Q / 9 picks the operand; Q % 9 < 8
+// is a code load of 8 rows x 128 bytes, one 16-byte chunk per lane (lane l
+// fills row l >> 3, slot l & 7 of the 8 rows with the chunk that belongs
+// there: the eight lanes of a row read one whole line); Q % 9 == 8 the
+// scales, 64 rows x 16 bytes.  Rows past the operand re-read its last row
+// (their results are never stored).  32-bit offsets: operands are below 4 GiB.
 template <int Q>
-__device__ __forceinline__ void rx_stage_one(const RxSrc& s, uint32_t u, uint32_t raw, int w, int lane) {
-  constexpr int op = Q / 6, i = Q % 6;
+__device__ __forceinline__ void rx_stage_one(const RxSrc& s, uint32_t p, uint32_t raw, int w, int lane) {
+  constexpr int op = Q / 9, i = Q % 9;
   const uint32_t base = op ? s.n0 : s.m0, last = op ? s.last_n : s.last_m;
   const uint32_t dst = raw + (uint32_t)(op * kRxOpB);
-  if constexpr (i < 4) {
-    const uint8_t* cq = (op ? s.b_codes : s.a_codes) + u * 64;
-    const int rr = i * 16 + (lane >> 2);                 // row within the wave's 64
-    const int c = (lane & 3) ^ rx_swz(rr);               // chunk held at slot lane & 3
+  if constexpr (i < 8) {
+    const uint8_t* cq = (op ? s.b_codes : s.a_codes) + p * kRxRowB;
+    const int rr = i * 8 + (lane >> 3);                  // row within the wave's 64
+    const int c = (lane & 7) ^ rx_swz(rr);               // chunk held at slot lane & 7
     const uint32_t gr = min(base + (uint32_t)(w * 64 + rr), last);
-    dma_to_lds<16>(cq, gr * s.code_ld + (uint32_t)(c * 16), dst + (uint32_t)((w * 64 + i * 16) * 64));
+    dma_to_lds<16>(cq, gr * s.code_ld + (uint32_t)(c * 16), dst + (uint32_t)((w * 64 + i * 8) * kRxRowB));
   } else {
-    const uint8_t* sq = (op ? s.b_scales : s.a_scales) + u * 8;
-    const uint32_t gr = min(base + (uint32_t)(w * 64 + (i - 4) * 32 + (lane >> 1)), last);
-    dma_to_lds<4>(sq, gr * s.scale_ld + (uint32_t)(lane & 1) * 4,
-                  dst + (uint32_t)(kRxCodeB + (w * 64 + (i - 4) * 32) * 8));
+    const uint8_t* sq = (op ? s.b_scales : s.a_scales) + p * 16;
+    const uint32_t gr = min(base + (uint32_t)(w * 64 + lane), last);
+    dma_to_lds<16>(sq, gr * s.scale_ld, dst + (uint32_t)(kRxCodeB + w * 64 * 16));
   }
 }
 
-// All 12 loads of a unit at once (prologue).
+// All 18 loads of a pair at once (prologue).
 template <int Q = 0>
-__device__ __forceinline__ void rx_stage(const RxSrc& s, uint32_t u, uint32_t raw, int w, int lane) {
-  if constexpr (Q < 12) {
-    rx_stage_one<Q>(s, u, raw, w, lane);
-    rx_stage<Q + 1>(s, u, raw, w, lane);
+__device__ __forceinline__ void rx_stage(const RxSrc& s, uint32_t p, uint32_t raw, int w, int lane) {
+  if constexpr (Q < 18) {
+    rx_stage_one<Q>(s, p, raw, w, lane);
+    rx_stage<Q + 1>(s, p, raw, w, lane);
   }
 }
 
-// Where in a unit (slot 64 ks + k of its 256) the 12 loads of the unit three
-// ahead are issued: load Q at slot 21 Q + 10, spread out so that no slot
+// Where in an odd unit (slot 64 ks + k of its 256) the 18 loads of the pair
+// two ahead are issued: load Q at slot 14 Q + 10, spread out so that no slot
 // waits for a burst of loads to be accepted.
 __host__ __device__ constexpr int rx_ld_at(int KS, int K) {
   const int x = KS * 64 + K - 10;
-  return (x >= 0 && x % 21 == 0 && x / 21 < 12) ? x / 21 : -1;
+  return (x >= 0 && x % 14 == 0 && x / 14 < 18) ? x / 14 : -1;
 }
 
 struct RxLd {
   const RxSrc* s;
-  uint32_t u, raw;     // unit to load and its buffer
+  uint32_t u, raw;     // pair to load and its buffer
   int w, lane;
 };
 
@@ -145,12 +154,13 @@ __device__ __forceinline__ void rx_mfma(floatx4& acc, const halfx8& a, const hal
   asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// Per-lane LDS offsets, fixed for the kernel: tile T (0-7 A tiles of the
-// wave's rows, 8-15 B tiles of its columns) adds (T & 7) * 1024 to the code
-// offsets and (T & 7) * 128 to the scale offsets (16 rows per tile).
+// Per-lane LDS offsets in a pair buffer, fixed for the kernel: tile T (0-7 A
+// tiles of the wave's rows, 8-15 B tiles of its columns) adds (T & 7) * 2048
+// to the code offsets and (T & 7) * 256 to the scale offsets (16 rows per
+// tile); the second unit of the pair adds 8 to the scale offsets.
 struct RxLane {
-  int ca, cb;          // chunk g of row (lane & 15) of A / B tile 0 (16 bytes: the four steps)
-  int sa, sb;          // the two scale bytes 2 g, 2 g + 1 of those rows
+  int ca[2], cb[2];    // chunk 4 P + g of row (lane & 15) of A / B tile 0 for the unit of parity P
+  int sa, sb;          // the two scale bytes 2 g, 2 g + 1 of those rows (first unit)
 };
 
 // Registers of the pipeline (indices are compile-time after unrolling).  The
@@ -221,12 +231,12 @@ __host__ __device__ constexpr int rx_cread(int KS, int K) {
   }
   return -1;
 }
-template <int KS, int K>
+template <int NP, int KS, int K>
 __device__ __forceinline__ void rx_reads(RxRegs& r, const uint8_t* ucur, const uint8_t* unxt,
                                          const RxLane& ln) {
   if constexpr (rx_cread(KS, K) >= 0) {
     constexpr int T = rx_cread(KS, K);
-    const uint4 q = *reinterpret_cast<const uint4*>(unxt + (T < 8 ? ln.ca : ln.cb) + (T & 7) * 1024);
+    const uint4 q = *reinterpret_cast<const uint4*>(unxt + (T < 8 ? ln.ca[NP] : ln.cb[NP]) + (T & 7) * 2048);
     r.cw[T][0] = q.x;
     r.cw[T][1] = q.y;
     r.cw[T][2] = q.z;
@@ -234,7 +244,7 @@ __device__ __forceinline__ void rx_reads(RxRegs& r, const uint8_t* ucur, const u
   }
   if constexpr (KS == 2 && (K & 1) == 1 && K < 32) {
     constexpr int T = K >> 1;
-    r.sraw[T] = *reinterpret_cast<const uint16_t*>(unxt + (T < 8 ? ln.sa : ln.sb) + (T & 7) * 128);
+    r.sraw[T] = *reinterpret_cast<const uint16_t*>(unxt + (T < 8 ? ln.sa : ln.sb) + NP * 8 + (T & 7) * 256);
   }
 }
 
@@ -258,7 +268,7 @@ __device__ __forceinline__ void rx_step(floatx4 (&acc)[8][8], RxRegs& r, const u
     constexpr int NKS = (KS + 1) & 3, NUP = KS == 3 ? (UP ^ 1) : UP, q = K - 56;
     rx_pair_to<NUP, NKS, (8 + (q >> 2)), (q & 3), 2>(r, r.nb[q >> 2]);
   }
-  rx_reads<KS, K>(r, ucur, unxt, ln);
+  rx_reads<UP ^ 1, KS, K>(r, ucur, unxt, ln);
   // the next unit's scale pairs, 16 steps after their reads
   if constexpr (KS == 2 && K >= 34 && K < 50)
     r.pr[UP ^ 1][K - 34] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sraw[K - 34], 128.0f, false);
@@ -294,17 +304,27 @@ template <int UP, bool LOADS>
 __device__ __forceinline__ void rx_unit(floatx4 (&acc)[8][8], RxRegs& r, uint8_t* smem,
                                         uint32_t smem_lds, const RxSrc& s, int U, int NU, int w,
                                         int lane, const RxLane& ln) {
-  if (U + 2 < NU) wait_vmcnt<kRxLoadsPerUnit>();
-  else wait_vmcnt<0>();
+  // unit U + 1 landed: an even unit may leave the pair the odd unit before it
+  // issued (units U + 2, U + 3) in flight; an odd unit's next unit belongs to
+  // the last pair issued
+  if constexpr (UP == 0) {
+    if (U + 2 < NU) wait_vmcnt<kRxLoadsPerPair>();
+    else wait_vmcnt<0>();
+  } else {
+    wait_vmcnt<0>();
+  }
   lds_barrier();
+  // an odd unit issues pair (U + 3) / 2 (units U + 3, U + 4) into the buffer
+  // of units U - 1, U, which every wave has finished reading (the codes and
+  // scales of a unit are read during the unit before it)
   RxLd ld;
   ld.s = &s;
-  ld.u = (uint32_t)(U + 3);
-  ld.raw = smem_lds + (uint32_t)(((U + 3) & 3) * kRxUnitB);
+  ld.u = (uint32_t)((U + 3) >> 1);
+  ld.raw = smem_lds + (uint32_t)((((U + 3) >> 1) & 1) * kRxUnitB);
   ld.w = w;
   ld.lane = lane;
-  const uint8_t* ucur = smem + (U & 3) * kRxUnitB;
-  const uint8_t* unxt = smem + ((U + 1 < NU ? U + 1 : NU - 1) & 3) * kRxUnitB;
+  const uint8_t* ucur = smem + ((U >> 1) & 1) * kRxUnitB;
+  const uint8_t* unxt = smem + (((U + 1 < NU ? U + 1 : NU - 1) >> 1) & 1) * kRxUnitB;
   // the VALU writes of the fragments expanded last need a few wait states
   // before an MFMA reads them (the compiler does not track hazards into
   // inline assembly)
@@ -365,11 +385,14 @@ void k_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
   RxLane ln;
   {
     const int r16 = lane & 15, g = lane >> 4;
-    const int chunk = (g ^ rx_swz(r16)) << 4;            // rows 16 i + r16 share swz(r16)
-    ln.ca = (wm * 128 + r16) * 64 + chunk;
-    ln.cb = kRxOpB + (wn * 128 + r16) * 64 + chunk;
-    ln.sa = kRxCodeB + (wm * 128 + r16) * 8 + 2 * g;
-    ln.sb = kRxOpB + kRxCodeB + (wn * 128 + r16) * 8 + 2 * g;
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+      const int chunk = ((4 * P + g) ^ rx_swz(r16)) << 4;  // rows 16 i + r16 share swz(r16)
+      ln.ca[P] = (wm * 128 + r16) * kRxRowB + chunk;
+      ln.cb[P] = kRxOpB + (wn * 128 + r16) * kRxRowB + chunk;
+    }
+    ln.sa = kRxCodeB + (wm * 128 + r16) * 16 + 2 * g;
+    ln.sb = kRxOpB + kRxCodeB + (wn * 128 + r16) * 16 + 2 * g;
   }
 
   floatx4 acc[8][8];
@@ -378,41 +401,38 @@ void k_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
 #pragma unroll
     for (int jn = 0; jn < 8; ++jn) acc[i][jn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // prologue: units 0-2 in flight; unit 0's codes and scales in registers;
-  // the A tiles and first two B tiles of step 0 expanded
+  // prologue: pairs 0 and 1 (units 0-3) in flight; unit 0's codes and
+  // scales in registers; the A tiles and first two B tiles of step 0 expanded
   RxRegs r;
   rx_stage(s, 0, smem_lds, w, lane);
-  if (NU > 1) rx_stage(s, 1, smem_lds + kRxUnitB, w, lane);
-  if (NU > 2) rx_stage(s, 2, smem_lds + 2 * kRxUnitB, w, lane);
-  // units 0 and 1 landed (at most one unit's loads still outstanding)
-  if (NU > 1) wait_vmcnt<kRxLoadsPerUnit>();
+  if (NU > 2) rx_stage(s, 1, smem_lds + kRxUnitB, w, lane);
+  // pair 0 landed (at most pair 1's loads still outstanding)
+  if (NU > 2) wait_vmcnt<kRxLoadsPerPair>();
   else wait_vmcnt<0>();
   lds_barrier();
 #pragma unroll
   for (int T = 0; T < 16; ++T) {
-    const uint4 q = *reinterpret_cast<const uint4*>(smem + (T < 8 ? ln.ca : ln.cb) + (T & 7) * 1024);
+    const uint4 q = *reinterpret_cast<const uint4*>(smem + (T < 8 ? ln.ca[0] : ln.cb[0]) + (T & 7) * 2048);
     r.cw[T][0] = q.x;
     r.cw[T][1] = q.y;
     r.cw[T][2] = q.z;
     r.cw[T][3] = q.w;
     r.pr[0][T] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-        *reinterpret_cast<const uint16_t*>(smem + (T < 8 ? ln.sa : ln.sb) + (T & 7) * 128), 128.0f, false);
+        *reinterpret_cast<const uint16_t*>(smem + (T < 8 ? ln.sa : ln.sb) + (T & 7) * 256), 128.0f, false);
   }
   rx_prologue_tiles<0>(r);
 
-  // units whose unit three ahead exists issue its loads; NU is even
+  // odd units whose pair two ahead exists (units U + 3, U + 4) issue its
+  // loads; NU is even
   int U = 0;
   for (; U + 4 < NU; U += 2) {
-    rx_unit<0, true>(acc, r, smem, smem_lds, s, U, NU, w, lane, ln);
+    rx_unit<0, false>(acc, r, smem, smem_lds, s, U, NU, w, lane, ln);
     rx_unit<1, true>(acc, r, smem, smem_lds, s, U + 1, NU, w, lane, ln);
   }
-  if (U + 3 < NU) {
-    rx_unit<0, true>(acc, r, smem, smem_lds, s, U, NU, w, lane, ln);
+  for (; U < NU; U += 2) {
+    rx_unit<0, false>(acc, r, smem, smem_lds, s, U, NU, w, lane, ln);
     rx_unit<1, false>(acc, r, smem, smem_lds, s, U + 1, NU, w, lane, ln);
-    U += 2;
   }
-  rx_unit<0, false>(acc, r, smem, smem_lds, s, U, NU, w, lane, ln);
-  rx_unit<1, false>(acc, r, smem, smem_lds, s, U + 1, NU, w, lane, ln);
 
   // every wave is done with the unit buffers (the epilogue reuses the LDS),
   // and the last MFMAs' results have reached the accumulator registers
@@ -547,7 +567,7 @@ int gemm_nvfp4_rx_split(int64_t M, int64_t N, int64_t K, int cus) {
 bool gemm_nvfp4_rx_fits(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                         const uint8_t* bc, const uint8_t* bs) {
   const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
-  return K > 0 && K % 256 == 0 && al(ac, 16) && al(bc, 16) && al(as, 4) && al(bs, 4) &&
+  return K > 0 && K % 256 == 0 && al(ac, 16) && al(bc, 16) && al(as, 16) && al(bs, 16) &&
          M * (K / 2) < ((int64_t)1 << 32) && N * (K / 2) < ((int64_t)1 << 32);
 }
 
