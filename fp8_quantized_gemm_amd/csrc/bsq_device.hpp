@@ -196,39 +196,51 @@ __device__ __forceinline__ float dpp_xor1f(float v) { return u2f(dpp_xor1(f2u(v)
 struct U4 {
   uint32_t x, y, z, w;
 };
-__device__ __forceinline__ U4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                       uint32_t k0, uint32_t k1) {
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                             uint32_t k0, uint32_t k1) {
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+  // three-input XORs as single v_bitop3_b32 (truth table 0x96)
+  const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+  const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+  c0 = n0;
+  c1 = (uint32_t)p1;
+  c2 = n2;
+  c3 = (uint32_t)p0;
+}
+
+// The four output words, each bitwise complemented (~x, ~y, ~z, ~w): the
+// stochastic-rounding pack below takes 65535 - r16 = ~r16, and the last
+// round's three-input XORs give ~x and ~z at no cost (truth table 0x69).
+__device__ __forceinline__ U4 philox10_not(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                           uint32_t k0, uint32_t k1) {
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    // three-input XORs as single v_bitop3_b32 (truth table 0x96)
-    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
-    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
-    c0 = n0;
-    c1 = (uint32_t)p1;
-    c2 = n2;
-    c3 = (uint32_t)p0;
+  for (int r = 0; r < 9; ++r) {
+    philox_round(c0, c1, c2, c3, k0, k1);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
-  return U4{c0, c1, c2, c3};
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+  const uint32_t nx = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x69);
+  const uint32_t nz = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x69);
+  return U4{nx, ~(uint32_t)p1, nz, ~(uint32_t)p0};
 }
 
-// Eight 16-bit random words for elements idx = 8*grp + j, j = 0..7 (word j>>1,
-// low half for even j).
+// Eight 16-bit random words for elements idx = 8*grp + j, j = 0..7 (Philox
+// output word j>>1, low half for even j), held complemented: nw[k] = ~word k,
+// so the half of element j is 65535 - r16(j).
 struct R16x8 {
-  uint32_t w[4];
-  __device__ __forceinline__ uint32_t get(int j) const { return (w[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu; }
+  uint32_t nw[4];
 };
 __device__ __forceinline__ R16x8 sr_words(uint64_t grp, uint64_t seed, uint32_t offset, uint32_t stream) {
-  const U4 r = philox10((uint32_t)grp, (uint32_t)(grp >> 32), offset, stream,
-                        (uint32_t)seed, (uint32_t)(seed >> 32));
+  const U4 r = philox10_not((uint32_t)grp, (uint32_t)(grp >> 32), offset, stream,
+                            (uint32_t)seed, (uint32_t)(seed >> 32));
   R16x8 o;
-  o.w[0] = r.x;
-  o.w[1] = r.y;
-  o.w[2] = r.z;
-  o.w[3] = r.w;
+  o.nw[0] = r.x;
+  o.nw[1] = r.y;
+  o.nw[2] = r.z;
+  o.nw[3] = r.w;
   return o;
 }
 
@@ -244,26 +256,49 @@ __device__ __forceinline__ R16x8 sr_words(uint64_t grp, uint64_t seed, uint32_t 
 // pair (bits 30..9 for the second), saturating at 6 and keeping the sign
 // (measured on 2^21 random inputs against that formula, no mismatch).  With
 // R = (65535 - r16) << 6 the carry happens iff r16 < floor(frac * 2^16), which
-// is the rule above bit for bit.  The two halves of a pair would share most of
-// R's bits, so each pair is converted twice, once with the even element's R
-// and once with the odd element's, and the low nibble of the first result is
-// merged with the high nibble of the second.  Only byte 0 of each result is
-// defined here (the instruction leaves the other bytes of its destination
-// unspecified), so the four pair bytes are gathered with byte permutes.
-__device__ __forceinline__ uint32_t fp4x8_sr(const float (&v)[8], const R16x8& rnd) {
+// is the rule above bit for bit.  The two random fields of one instruction
+// overlap, so each pair is converted twice: once with the even element's
+// 65535 - r16 in bits 31..16 (bits 15..0 zero), once with the odd element's
+// in bits 30..15 (bits 14..0 zero).  The instruction writes only the byte its
+// op_sel names and keeps the other three, so pair k's two conversions go to
+// byte k of two words, e (even nibbles valid) and o (odd nibbles valid), and
+// one bitwise select merges them.  Written as inline assembly with the words
+// as tied operands: the compiler's builtin does not tie the kept bytes.  The
+// s_nop after each conversion gives the wait state a VALU read of a
+// byte-selected destination needs, which the compiler cannot insert for
+// inline assembly.
+template <int K>
+__device__ __forceinline__ void sr_pk_fp4_byte(uint32_t& dst, float a, float b, uint32_t rnd) {
   typedef float f2 __attribute__((ext_vector_type(2)));
-  uint32_t b[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t nw = ~rnd.w[k];                       // 65535 - r16 in both halves
-    const f2 pr = {v[2 * k], v[2 * k + 1]};
-    const uint32_t e = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pr, nw << 16, 1.0f, 0);
-    const uint32_t o = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pr, (nw >> 1) & 0x7FFF8000u, 1.0f, 0);
-    b[k] = (e & 0x0Fu) | (o & 0xF0u);                    // even from e (R bits 31..10), odd from o (30..9)
+  const f2 pr = {a, b};
+  if constexpr (K == 0)   // bytes 1-3 are written by the later conversions
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0\n\ts_nop 0" : "=v"(dst) : "v"(pr), "v"(rnd));
+  else if constexpr (K == 1)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]\n\ts_nop 0"
+                 : "+v"(dst) : "v"(pr), "v"(rnd));
+  else if constexpr (K == 2)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]\n\ts_nop 0"
+                 : "+v"(dst) : "v"(pr), "v"(rnd));
+  else
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]\n\ts_nop 0"
+                 : "+v"(dst) : "v"(pr), "v"(rnd));
+}
+
+template <int K = 0>
+__device__ __forceinline__ void fp4x8_sr_pairs(const float (&v)[8], const R16x8& rnd, uint32_t& e,
+                                               uint32_t& o) {
+  if constexpr (K < 4) {
+    const uint32_t nw = rnd.nw[K];
+    sr_pk_fp4_byte<K>(e, v[2 * K], v[2 * K + 1], nw << 16);
+    sr_pk_fp4_byte<K>(o, v[2 * K], v[2 * K + 1], (nw >> 1) & 0x7FFF8000u);
+    fp4x8_sr_pairs<K + 1>(v, rnd, e, o);
   }
-  const uint32_t b01 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
-  const uint32_t b23 = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);
-  return __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+}
+
+__device__ __forceinline__ uint32_t fp4x8_sr(const float (&v)[8], const R16x8& rnd) {
+  uint32_t e, o;
+  fp4x8_sr_pairs<0>(v, rnd, e, o);
+  return (e & 0x0F0F0F0Fu) | (o & 0xF0F0F0F0u);   // one bitfield insert
 }
 
 }  // namespace bsq
