@@ -350,6 +350,12 @@ void k_gemm_mx_rx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const
   // MFMAs' results have reached the accumulator registers
   lds_barrier();
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // the accumulators count as written here: no read of them moves above the
+  // barrier and the wait states
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
   __builtin_amdgcn_sched_barrier(0);
 
   // epilogue: alpha * acc -> BF16 (RNE), staged per wave through LDS so that
