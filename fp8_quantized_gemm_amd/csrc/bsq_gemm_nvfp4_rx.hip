@@ -41,16 +41,17 @@
 //    before each; one workgroup barrier per unit makes a landed unit visible
 //    to all waves;
 //  * each tile's 16 code bytes for the unit (its four steps) are read from
-//    LDS in one piece, as soon as the previous unit's last expansion from
-//    them is done, about a step ahead of their first use; the scales of
-//    U + 1 during step 2;
-//  * during step ks: B tile n of step ks is expanded just in time (during the
-//    MFMAs of B tile n - 1), and the eight A tiles and first two B tiles of
-//    step ks + 1 are expanded for the next step.
-// Fragments are written by VALU operations and read by MFMAs written as
-// inline assembly, so the compiler's hazard recognizer does not see those
-// dependencies: every fragment is complete at least one MFMA before its first
-// reader, and explicit s_nop cover the register copies at step boundaries.
+//    LDS in one piece during steps 2-3 of the unit before, once that unit's
+//    last expansion from them is done; the scales of U + 1 are read in step
+//    0 of U and converted in step 1;
+//  * during step ks: exactly one expansion pair (two VALU operations) after
+//    each MFMA, written with the MFMA as one assembly block: the eight A
+//    tiles and B tiles 0-6 of step ks + 1 (B tile n in place, once step ks
+//    has read it), and B tile 7 of step ks itself (see rx_slot).
+// Fragments are written and read inside inline assembly, so the compiler's
+// hazard recognizer does not see those dependencies: every fragment is
+// complete at least two MFMAs before its first reader and is rewritten no
+// earlier than two MFMAs after its last.
 // LDS code rows are 128 bytes (a pair): the 16-byte chunk c of row r sits at
 // slot c ^ swz(r), swz(r) = (r >> 1) & 7.  A 16-byte read is served sixteen
 // lanes (sixteen consecutive rows, one chunk) per cycle by 64 four-byte banks;
@@ -105,21 +106,29 @@ struct RxSrc {
 // there: the eight lanes of a row read one whole line); Q % 9 == 8 the
 // scales, 64 rows x 16 bytes.  Rows past the operand re-read its last row
 // (their results are never stored).  32-bit offsets: operands are below 4 GiB.
+// One direct load of 16 bytes per lane into LDS at M0 + 16 * lane, with M0
+// formed by a single scalar add of a compile-time offset to an LDS base.
+template <int IMM>
+__device__ __forceinline__ void rx_dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds), "n"(IMM) : "memory", "m0", "scc");
+}
+
 template <int Q>
 __device__ __forceinline__ void rx_stage_one(const RxSrc& s, uint32_t p, uint32_t raw, int w, int lane) {
   constexpr int op = Q / 9, i = Q % 9;
   const uint32_t base = op ? s.n0 : s.m0, last = op ? s.last_n : s.last_m;
-  const uint32_t dst = raw + (uint32_t)(op * kRxOpB);
   if constexpr (i < 8) {
     const uint8_t* cq = (op ? s.b_codes : s.a_codes) + p * kRxRowB;
     const int rr = i * 8 + (lane >> 3);                  // row within the wave's 64
     const int c = (lane & 7) ^ rx_swz(rr);               // chunk held at slot lane & 7
     const uint32_t gr = min(base + (uint32_t)(w * 64 + rr), last);
-    dma_to_lds<16>(cq, gr * s.code_ld + (uint32_t)(c * 16), dst + (uint32_t)((w * 64 + i * 8) * kRxRowB));
+    rx_dma16<op * kRxOpB + i * 8 * kRxRowB>(cq, gr * s.code_ld + (uint32_t)(c * 16),
+                                           raw + (uint32_t)(w * 64 * kRxRowB));
   } else {
     const uint8_t* sq = (op ? s.b_scales : s.a_scales) + p * 16;
     const uint32_t gr = min(base + (uint32_t)(w * 64 + lane), last);
-    dma_to_lds<16>(sq, gr * s.scale_ld, dst + (uint32_t)(kRxCodeB + w * 64 * 16));
+    rx_dma16<op * kRxOpB + kRxCodeB>(sq, gr * s.scale_ld, raw + (uint32_t)(w * 64 * 16));
   }
 }
 
@@ -146,14 +155,6 @@ struct RxLd {
   int w, lane;
 };
 
-// acc += srcA . srcB on the FP16 MFMA (16 x 16 output, K = 32), written out so
-// that each accumulator tile keeps one fixed quad of accumulator registers for
-// the whole kernel (tied input / output).  The operands are written by VALU
-// operations at least one MFMA earlier.
-__device__ __forceinline__ void rx_mfma(floatx4& acc, const halfx8& a, const halfx8& b) {
-  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
 // Per-lane LDS offsets in a pair buffer, fixed for the kernel: tile T (0-7 A
 // tiles of the wave's rows, 8-15 B tiles of its columns) adds (T & 7) * 2048
 // to the code offsets and (T & 7) * 256 to the scale offsets (16 rows per
@@ -171,10 +172,8 @@ struct RxRegs {
   uint32_t sraw[16];         // scale bytes 2 g, 2 g + 1 of the next unit, as read
   halfx2 pr[2][16];          // {S(2g), S(2g + 1)} * 2^7 per tile, units of parity 0 / 1
   halfx8 a[2][8];            // A fragments of the current step and the next
-  halfx8 b[8];               // B fragments of the current step
-  halfx8 nb[2];              // first two B fragments of the next step
-  uint32_t o[3][4];          // pairs of the fragment being expanded, per stream:
-                             // A tiles of the next step, B tile of this step, B tiles 0-1 of the next
+  halfx8 b[8];               // B fragments (tiles 0-6 rewritten for the next step once read)
+  uint32_t o[2][4];          // pairs of the fragment being expanded: A stream, B stream
 };
 
 // Pair SEL (0-3) of the expansion of tile T for step s (= KS of a unit of
@@ -194,46 +193,104 @@ __device__ __forceinline__ void rx_pair_to(RxRegs& r, halfx8& dst) {
   if constexpr (SEL == 3) dst = __builtin_bit_cast(halfx8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-// The A pairs of step ks + 1 go after steps rx_aq(q) (q = 0..31), spread over
-// steps 0..55; the B pairs of tile n (2..7) of step ks after steps
-// 8 (n - 1) + 0, 2, 4, 6; those of tiles 0 and 1 of step ks + 1 after steps
-// 56..63.
-__host__ __device__ constexpr int rx_aq(int q) { return (q * 55) / 31; }
-
-template <int UP, int KS, int K, int Q>
-__device__ __forceinline__ void rx_a_pairs(RxRegs& r) {
-  if constexpr (Q < 32) {
-    if constexpr (rx_aq(Q) == K) {
-      // step KS + 1 of this unit, or step 0 of the next (parity UP ^ 1)
-      constexpr int NKS = (KS + 1) & 3, NUP = KS == 3 ? (UP ^ 1) : UP;
-      rx_pair_to<NUP, NKS, (Q >> 2), (Q & 3), 0>(r, r.a[(KS + 1) & 1][Q >> 2]);
-    }
-    rx_a_pairs<UP, KS, K, Q + 1>(r);
+// MFMA and expansion pair as one assembly block: acc += s0 . s1 (the MFMA's
+// first operand is the B fragment, its second the A fragment), then
+// out = pair SEL of the code dword cw (byte SEL: two E2M1 codes, times 2^-14)
+// times the block scale, half H of p broadcast to both halves (the same two
+// operations as rx_pk).  Written together so that the compiler can neither
+// split the pair around the MFMA nor move it to another MFMA: left to
+// itself it placed one VALU operation between some MFMAs and three between
+// others, and a third operation between two MFMAs delays the second.
+// The pair is formed in its own output register (early clobber: written
+// before the scale is read), so that consecutive blocks share no register
+// that one writes and the next touches; the compiler, which cannot see into
+// the blocks, would otherwise put a wait state between them.
+#define BSQ_RX_MP(CVT_SEL, MUL_SEL)                                                            \
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %2, %3, %0\n\t"                                    \
+               "v_cvt_scalef32_pk_f16_fp4 %1, %4, %5" CVT_SEL "\n\t"                           \
+               "v_pk_mul_f16 %1, %6, %1" MUL_SEL                                                \
+               : "+a"(acc), "=&v"(out)                                                          \
+               : "v"(s0), "v"(s1), "v"(cw), "s"(k), "v"(p))
+template <int SEL, int H>
+__device__ __forceinline__ void rx_mfma_pair(floatx4& acc, const halfx8& s0, const halfx8& s1, uint32_t cw,
+                                             halfx2 p, uint32_t& out) {
+  const float k = 0x1p-14f;
+  if constexpr (H == 0) {
+    if constexpr (SEL == 0) BSQ_RX_MP("", " op_sel_hi:[0,1]");
+    else if constexpr (SEL == 1) BSQ_RX_MP(" op_sel:[1,0,0]", " op_sel_hi:[0,1]");
+    else if constexpr (SEL == 2) BSQ_RX_MP(" op_sel:[0,1,0]", " op_sel_hi:[0,1]");
+    else BSQ_RX_MP(" op_sel:[1,1,0]", " op_sel_hi:[0,1]");
+  } else {
+    if constexpr (SEL == 0) BSQ_RX_MP("", " op_sel:[1,0]");
+    else if constexpr (SEL == 1) BSQ_RX_MP(" op_sel:[1,0,0]", " op_sel:[1,0]");
+    else if constexpr (SEL == 2) BSQ_RX_MP(" op_sel:[0,1,0]", " op_sel:[1,0]");
+    else BSQ_RX_MP(" op_sel:[1,1,0]", " op_sel:[1,0]");
   }
 }
+#undef BSQ_RX_MP
 
-// LDS reads of step KS (after step K).  A tile's 16 code bytes (its four
-// steps of the unit) are read in one piece into cw[T] as soon as the current
-// unit's last expansion from them is done: A tiles after their last pair of
-// step 2 (for step 3), B tiles 0-1 after theirs (step 2, slots 59 and 63),
-// B tiles 2-7 after their just-in-time pairs of step 3; each about 57 steps
-// before the next unit's first expansion from them.  In step 2, the scale
-// bytes of the next unit (steps 1, 3, .., 31).
+// rx_pair_to with the MFMA of the slot fused in front (see rx_mfma_pair).
+template <int UP, int KS, int T, int SEL, int STREAM>
+__device__ __forceinline__ void rx_mfma_pair_to(floatx4& acc, const halfx8& fb, const halfx8& fa, RxRegs& r,
+                                                halfx8& dst) {
+  uint32_t (&o)[4] = r.o[STREAM];
+  rx_mfma_pair<SEL, (KS >> 1)>(acc, fb, fa, r.cw[T][KS], r.pr[UP][T], o[SEL]);
+  if constexpr (SEL == 3) dst = __builtin_bit_cast(halfx8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// Schedule of one step: MFMA k (0..63) multiplies B tile k >> 3 by A tile
+// k & 7, and exactly one expansion pair (two VALU operations) follows each
+// MFMA.  One wave per SIMD issues every instruction itself: between two
+// 16x16x32 FP16 MFMAs it has room for two more instructions at no cost, and
+// each further one, VALU or not, delays the next MFMA (register-only loops
+// of this MFMA ran at 99% of the MFMA-only rate with two VALU operations
+// after each, 77% with three, and 91% with four and none alternating).
+// During step s the wave expands every fragment step s + 1 needs except B
+// tile 7: the eight A tiles into the other A buffer and B tiles 0-6 in place,
+// each starting two MFMAs after step s has read it for the last time; B tile
+// 7 of step s itself is expanded after MFMAs 1-4 (step s - 1 read it last at
+// its MFMA 63):
+//   slot 0: A0 pair 0; slots 1-4: B7 (this step) pairs 0-3; 5-7: A0 pairs 1-3;
+//   even k >= 8: A tile k / 8, pair (k % 8) / 2;
+//   odd k >= 9: B tile (k - 9) / 8 of the next step, pair ((k - 9) % 8) / 2.
+// Every fragment is complete at least two MFMAs before its first reader.
+// Returns T * 4 + SEL (T 0-7 A tiles, 8-15 B tiles), plus 64 for B7 of this step.
+__host__ __device__ constexpr int rx_slot(int k) {
+  if (k == 0) return 0;
+  if (k <= 4) return 64 + 15 * 4 + (k - 1);
+  if (k <= 7) return k - 4;
+  if ((k & 1) == 0) return (k >> 3) * 4 + ((k & 7) >> 1);
+  return (8 + ((k - 9) >> 3)) * 4 + (((k - 9) & 7) >> 1);
+}
+
+// LDS code reads of the next unit (after MFMA K of step KS): a tile's 16 code
+// bytes for all four steps, read in one piece once the tile's last expansion
+// from the current unit's bytes is done (its step-3 pairs, placed in step 2,
+// B7 in step 3).  Step 2: A tiles 0-5 after MFMA 8 m + 8 and B tiles 0-4
+// after 8 n + 17 (their pairs end at 8 m + 7 and 8 n + 15); the wait at the
+// start of step 3 covers them.  Step 3: B7 after MFMA 5, then A6, B5, A7, B6
+// (whose step-2 pairs end at 54-63) after 7, 9, 11, 13; the compiler waits for
+// these before their first pairs at slots 48-57.  Returns the tile, or -1.
 __host__ __device__ constexpr int rx_cread(int KS, int K) {
   if (KS == 2) {
-    for (int T = 0; T < 8; ++T)
-      if (K == (4 * T + 3) * 55 / 31 + 1) return T;
-    if (K == 60) return 8;
+    if (K >= 8 && K <= 48 && (K & 7) == 0) return (K >> 3) - 1;
+    if (K >= 17 && K <= 49 && ((K - 17) & 7) == 0) return 8 + ((K - 17) >> 3);
   }
   if (KS == 3) {
-    if (K == 0) return 9;
-    if (K % 8 == 7 && K >= 15 && K <= 55) return 8 + (K + 1) / 8;
+    if (K == 5) return 15;
+    if (K == 7) return 6;
+    if (K == 9) return 13;
+    if (K == 11) return 7;
+    if (K == 13) return 14;
   }
   return -1;
 }
+
+// Reads after MFMA K of step KS: code reads (rx_cread) and, in step 0, the
+// scale bytes of the next unit (tile K / 2 after odd K < 32), converted in
+// step 1 after the same MFMAs.  NP is the next unit's parity in its pair.
 template <int NP, int KS, int K>
-__device__ __forceinline__ void rx_reads(RxRegs& r, const uint8_t* ucur, const uint8_t* unxt,
-                                         const RxLane& ln) {
+__device__ __forceinline__ void rx_reads(RxRegs& r, const uint8_t* unxt, const RxLane& ln) {
   if constexpr (rx_cread(KS, K) >= 0) {
     constexpr int T = rx_cread(KS, K);
     const uint4 q = *reinterpret_cast<const uint4*>(unxt + (T < 8 ? ln.ca[NP] : ln.cb[NP]) + (T & 7) * 2048);
@@ -242,56 +299,56 @@ __device__ __forceinline__ void rx_reads(RxRegs& r, const uint8_t* ucur, const u
     r.cw[T][2] = q.z;
     r.cw[T][3] = q.w;
   }
-  if constexpr (KS == 2 && (K & 1) == 1 && K < 32) {
+  if constexpr (KS == 0 && (K & 1) == 1 && K < 32) {
     constexpr int T = K >> 1;
     r.sraw[T] = *reinterpret_cast<const uint16_t*>(unxt + (T < 8 ? ln.sa : ln.sb) + NP * 8 + (T & 7) * 256);
   }
 }
 
-// Step K (0..63) of step KS of a unit of parity UP: MFMA K (B tile K >> 3 x A
-// tile K & 7), then the work placed after it.
+// MFMA K (0..63) of step KS of a unit of parity UP, then the work placed after it.
 template <int UP, bool LOADS, int KS, int K>
-__device__ __forceinline__ void rx_step(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* ucur,
-                                        const uint8_t* unxt, const RxLane& ln, const RxLd& ld) {
+__device__ __forceinline__ void rx_step(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* unxt,
+                                        const RxLane& ln, const RxLd& ld) {
   constexpr int n = K >> 3, mi = K & 7;
-  rx_mfma(acc[mi][n], r.b[n], r.a[KS & 1][mi]);
+  constexpr int e = rx_slot(K);
+  // the next step: step KS + 1 of this unit, or step 0 of the next (parity UP ^ 1)
+  constexpr int NKS = (KS + 1) & 3, NUP = KS == 3 ? (UP ^ 1) : UP;
+  floatx4& c = acc[mi][n];
+  const halfx8& fa = r.a[KS & 1][mi];
+  const halfx8& fb = r.b[n];
+  if constexpr (e >= 64)
+    rx_mfma_pair_to<UP, KS, 15, (e & 3), 1>(c, fb, fa, r, r.b[7]);
+  else if constexpr ((e >> 2) < 8)
+    rx_mfma_pair_to<NUP, NKS, (e >> 2), (e & 3), 0>(c, fb, fa, r, r.a[(KS + 1) & 1][e >> 2]);
+  else
+    rx_mfma_pair_to<NUP, NKS, (e >> 2), (e & 3), 1>(c, fb, fa, r, r.b[(e >> 2) - 8]);
   if constexpr (LOADS && rx_ld_at(KS, K) >= 0) rx_stage_one<rx_ld_at(KS, K)>(*ld.s, ld.u, ld.raw, ld.w, ld.lane);
-  // B tile n + 1 of this step, just in time (its last pair one MFMA before
-  // the MFMA that reads it: a VALU write needs wait states before an MFMA
-  // reads the register, and the compiler does not see into the MFMA asm)
-  if constexpr ((K & 1) == 0 && n + 1 >= 2 && n + 1 < 8)
-    rx_pair_to<UP, KS, (8 + n + 1), ((K & 7) >> 1), 1>(r, r.b[n + 1]);
-  // A tiles of the next step
-  rx_a_pairs<UP, KS, K, 0>(r);
-  // B tiles 0 and 1 of the next step
-  if constexpr (K >= 56) {
-    constexpr int NKS = (KS + 1) & 3, NUP = KS == 3 ? (UP ^ 1) : UP, q = K - 56;
-    rx_pair_to<NUP, NKS, (8 + (q >> 2)), (q & 3), 2>(r, r.nb[q >> 2]);
+  rx_reads<UP ^ 1, KS, K>(r, unxt, ln);
+  // the next unit's scale pairs (read in step 0)
+  if constexpr (KS == 1 && (K & 1) == 1 && K < 32) {
+    r.pr[UP ^ 1][K >> 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sraw[K >> 1], 128.0f, false);
+    asm volatile("" : "+v"(r.pr[UP ^ 1][K >> 1]));
   }
-  rx_reads<UP ^ 1, KS, K>(r, ucur, unxt, ln);
-  // the next unit's scale pairs, 16 steps after their reads
-  if constexpr (KS == 2 && K >= 34 && K < 50)
-    r.pr[UP ^ 1][K - 34] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sraw[K - 34], 128.0f, false);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int UP, bool LOADS, int KS, int K>
-__device__ __forceinline__ void rx_steps(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* ucur,
-                                         const uint8_t* unxt, const RxLane& ln, const RxLd& ld) {
+__device__ __forceinline__ void rx_steps(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* unxt,
+                                         const RxLane& ln, const RxLd& ld) {
   if constexpr (K < 64) {
-    rx_step<UP, LOADS, KS, K>(acc, r, ucur, unxt, ln, ld);
-    rx_steps<UP, LOADS, KS, K + 1>(acc, r, ucur, unxt, ln, ld);
+    rx_step<UP, LOADS, KS, K>(acc, r, unxt, ln, ld);
+    rx_steps<UP, LOADS, KS, K + 1>(acc, r, unxt, ln, ld);
   }
 }
 
 template <int UP, bool LOADS, int KS>
-__device__ __forceinline__ void rx_kstep(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* ucur,
-                                         const uint8_t* unxt, const RxLane& ln, const RxLd& ld) {
-  rx_steps<UP, LOADS, KS, 0>(acc, r, ucur, unxt, ln, ld);
-  r.b[0] = r.nb[0];
-  r.b[1] = r.nb[1];
-  // wait states between these VALU copies and the next step's first MFMA
-  asm volatile("s_nop 4" ::: "memory");
+__device__ __forceinline__ void rx_kstep(floatx4 (&acc)[8][8], RxRegs& r, const uint8_t* unxt,
+                                         const RxLane& ln, const RxLd& ld) {
+  // every LDS read issued before this step has completed (lgkmcnt(0) through
+  // the builtin, so the compiler knows and places no waits for them later);
+  // the reads of a step are issued at least 14 MFMAs before its end
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  rx_steps<UP, LOADS, KS, 0>(acc, r, unxt, ln, ld);
 }
 
 // Unit U (parity UP): make unit U + 1 visible to every wave (this wave's own
@@ -327,23 +384,18 @@ __device__ __forceinline__ void rx_unit(floatx4 (&acc)[8][8], RxRegs& r, uint8_t
   ld.raw = smem_lds + (uint32_t)((((U + 3) >> 1) & 1) * kRxUnitB);
   ld.w = w;
   ld.lane = lane;
-  const uint8_t* ucur = smem + ((U >> 1) & 1) * kRxUnitB;
   const uint8_t* unxt = smem + (((U + 1 < NU ? U + 1 : NU - 1) >> 1) & 1) * kRxUnitB;
-  // the VALU writes of the fragments expanded last need a few wait states
-  // before an MFMA reads them (the compiler does not track hazards into
-  // inline assembly)
-  asm volatile("s_nop 4" ::: "memory");
-  rx_kstep<UP, LOADS, 0>(acc, r, ucur, unxt, ln, ld);
-  rx_kstep<UP, LOADS, 1>(acc, r, ucur, unxt, ln, ld);
-  rx_kstep<UP, LOADS, 2>(acc, r, ucur, unxt, ln, ld);
-  rx_kstep<UP, LOADS, 3>(acc, r, ucur, unxt, ln, ld);
+  rx_kstep<UP, LOADS, 0>(acc, r, unxt, ln, ld);
+  rx_kstep<UP, LOADS, 1>(acc, r, unxt, ln, ld);
+  rx_kstep<UP, LOADS, 2>(acc, r, unxt, ln, ld);
+  rx_kstep<UP, LOADS, 3>(acc, r, unxt, ln, ld);
 }
 
-// Expansion of the A tiles (into a[0]) and the first two B tiles (into b) of
-// step 0 of unit 0 (prologue), from cw[T][0] and pr[0].
+// Expansion of the A tiles (into a[0]) and B tiles 0-6 (into b) of step 0
+// of unit 0 (prologue), from cw[T][0] and pr[0]; B tile 7 follows in step 0.
 template <int T>
 __device__ __forceinline__ void rx_prologue_tiles(RxRegs& r) {
-  if constexpr (T < 10) {
+  if constexpr (T < 15) {
     halfx8& d = T < 8 ? r.a[0][T & 7] : r.b[T & 7];
     rx_pair_to<0, 0, T, 0, 0>(r, d);
     rx_pair_to<0, 0, T, 1, 0>(r, d);
