@@ -324,6 +324,9 @@ __device__ __forceinline__ void rx_step(floatx4 (&acc)[8][8], RxRegs& r, const u
     rx_mfma_pair_to<NUP, NKS, (e >> 2), (e & 3), 1>(c, fb, fa, r, r.b[(e >> 2) - 8]);
   if constexpr (LOADS && rx_ld_at(KS, K) >= 0) rx_stage_one<rx_ld_at(KS, K)>(*ld.s, ld.u, ld.raw, ld.w, ld.lane);
   rx_reads<UP ^ 1, KS, K>(r, unxt, ln);
+  // step 3: the reads issued after MFMAs 5-13 have completed before the
+  // first pairs that use them (slots 48-57): one wait instead of four
+  if constexpr (KS == 3 && K == 40) __builtin_amdgcn_s_waitcnt(0xC07F);
   // the next unit's scale pairs (read in step 0)
   if constexpr (KS == 1 && (K & 1) == 1 && K < 32) {
     r.pr[UP ^ 1][K >> 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sraw[K >> 1], 128.0f, false);
@@ -357,24 +360,21 @@ __device__ __forceinline__ void rx_kstep(floatx4 (&acc)[8][8], RxRegs& r, const 
 // U + 3 is past the last unit) issue unit U + 3 into the buffer of unit U - 1
 // on the way.  Past the last unit, the next-unit reads fetch the last unit
 // again (its buffer is never refilled), which keeps the steps branch-free.
-// (Only the odd units' barriers are needed: an even unit reads unit U + 1
-// from its own pair, made visible by the previous odd unit's barrier, and
-// issues no loads.  Dropping the even units' barriers measured within
-// +-1.5% by shape and 0.0% over the six 8B GEMMs, so they stay.)
+// Only odd units synchronise: an odd unit reads unit U + 1, the first unit
+// of the pair issued two units before it, so it waits for all of its own
+// loads and passes a barrier, after which every wave's loads of that pair
+// have landed and every wave has finished reading units U - 1 and U (read
+// during the units before them), whose buffer its loads then refill.  An
+// even unit reads unit U + 1 from its own pair, made visible by the previous
+// odd unit's barrier (the prologue's for unit 1), and issues no loads.
 template <int UP, bool LOADS>
 __device__ __forceinline__ void rx_unit(floatx4 (&acc)[8][8], RxRegs& r, uint8_t* smem,
                                         uint32_t smem_lds, const RxSrc& s, int U, int NU, int w,
                                         int lane, const RxLane& ln) {
-  // unit U + 1 landed: an even unit may leave the pair the odd unit before it
-  // issued (units U + 2, U + 3) in flight; an odd unit's next unit belongs to
-  // the last pair issued
-  if constexpr (UP == 0) {
-    if (U + 2 < NU) wait_vmcnt<kRxLoadsPerPair>();
-    else wait_vmcnt<0>();
-  } else {
+  if constexpr (UP == 1) {
     wait_vmcnt<0>();
+    lds_barrier();
   }
-  lds_barrier();
   // an odd unit issues pair (U + 3) / 2 (units U + 3, U + 4) into the buffer
   // of units U - 1, U, which every wave has finished reading (the codes and
   // scales of a unit are read during the unit before it)
