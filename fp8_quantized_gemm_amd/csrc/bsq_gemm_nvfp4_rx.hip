@@ -38,8 +38,8 @@
 //    rows 64 w .. 64 w + 63; an odd unit U issues pair (U + 3) / 2, its 18
 //    loads spread over the unit's 256 MFMAs (one every 14), into the buffer
 //    of units U - 1 and U, whose codes and scales were read during the unit
-//    before each; one workgroup barrier per unit makes a landed unit visible
-//    to all waves;
+//    before each; one workgroup barrier per pair (at odd units) makes a
+//    landed pair visible to all waves;
 //  * each tile's 16 code bytes for the unit (its four steps) are read from
 //    LDS in one piece during steps 2-3 of the unit before, once that unit's
 //    last expansion from them is done; the scales of U + 1 are read in step
