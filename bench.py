@@ -92,6 +92,11 @@ class Flusher:
         torch.sum(self.buf, dtype=torch.int64)
 
 
+def progress(msg):
+    """One line on stderr as each part of the run finishes."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def median(v):
     v = sorted(v)
     n = len(v)
@@ -773,6 +778,7 @@ def main():
     step, ms_list, per, wall = run_step_bench(args.workload, not args.no_rht, dev, args.steps,
                                               args.warmup, flush, bx=not args.no_bx)
     ms = median(ms_list)
+    progress(f"{args.workload} step: {ms:.3f} ms")
 
     # the same step with RHT off on the WGRAD operands (only the quantizers change)
     step.rht = 1 - step.rht
@@ -820,15 +826,20 @@ def main():
             "value": round(step.flops / (ms_other * 1e-3) / 1e12, 2)},
         "wall_s": round(wall, 3),
     }
+    progress("step with the other RHT setting done")
     if not args.no_fp8:
         out["fp8_baseline"] = fp8_baseline(step, args.steps, args.warmup, ms, flush)
+        progress("FP8 baseline done")
     if not args.no_vendor_fp16:
         out["vendor_fp16_gemm"] = vendor_fp16_gemm(step, step.flops / (gemm_tflops * 1e12) * 1e3, flush)
+        progress("vendor FP16 GEMM done")
     if not args.no_swiglu:
         out["swiglu_fused_quantize"] = swiglu_fused(step)
         out["mlp_layer_step"] = mlp_layer_step(step, args.steps, args.warmup)
+        progress("SwiGLU and MLP-layer step done")
     if args.workload == "8b":
         out["rht_wgrad_error"] = rht_wgrad_error(step)
+        progress("RHT error done")
     del step
     torch.cuda.empty_cache()
     if args.workload == "8b" and not args.no_405b:
@@ -845,14 +856,18 @@ def main():
             "gemm_frac_of_fp16_peak": round(g_tf / PEAK_FP16_TFLOPS, 4), "breakdown": bd}
         del s405
         torch.cuda.empty_cache()
+        progress("405b step done")
     if not args.no_tiny:
         out["tiny_fprop_256"] = tiny_fprop(dev)
     if not args.no_mx:
         out["mx_square_4096"] = mx_square(dev)
+        progress("MX 4096^3 done")
     if not args.no_route_ceiling:
         out["nvfp4_route_ceilings"] = route_ceilings(dev)
+        progress("route ceilings done")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, not args.no_rht)
+        progress("CPU baseline done")
     print(json.dumps(out))
 
 
