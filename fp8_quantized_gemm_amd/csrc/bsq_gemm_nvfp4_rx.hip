@@ -458,7 +458,7 @@ void k_gemm_nvfp4_rx(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
     for (int jn = 0; jn < 8; ++jn) acc[i][jn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // prologue: pairs 0 and 1 (units 0-3) in flight; unit 0's codes and
-  // scales in registers; the A tiles and first two B tiles of step 0 expanded
+  // scales in registers; the A tiles and B tiles 0-6 of step 0 expanded
   RxRegs r;
   rx_stage(s, 0, smem_lds, w, lane);
   if (NU > 2) rx_stage(s, 1, smem_lds + kRxUnitB, w, lane);
