@@ -304,12 +304,25 @@ __global__ __launch_bounds__(256) void k_amax_tile_rht(const uint16_t* __restric
 constexpr int kSwigluBlocks = 1024;                    // 4 workgroups per CU
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// ln 2 split for the argument reduction (Cody and Waite): the high part has
+// 16 significant bits, so n * kLn2Hi is exact for |n| < 2^8.
+constexpr float kLn2Hi = 0.693145751953125f;
+constexpr float kLn2Lo = 1.42860682030941723212e-6f;
+
 // sigma(g) and sigma(-g) = 1 - sigma(g), each without cancellation, from
-// e = exp(-|g|) (never overflows; the exp2 lowering keeps denormal results).
-// Relative error a few FP32 ulps (|g| log2(e) rounding, v_exp, v_rcp).
+// e = exp(-|g|) (never overflows).  The argument is reduced first, |g| =
+// n ln 2 + r with |r| <= ln2 / 2 (n = rint(|g| log2 e), r by two FMAs), and
+// e = 2^-n exp(-r): the exponential's argument then carries no rounding error
+// that grows with |g|, and the relative error stays at a few FP32 ulps (v_exp
+// on a small argument, v_rcp) for every gate; 2^-n is an exact exponent
+// shift, rounding once where e falls below the normal range.
 struct SigPair { float s, c; };
 __device__ __forceinline__ SigPair sigmoid_pair(float g) {
-  const float e = exp2f(-fabsf(g) * kLog2e);
+  const float a = fabsf(g);
+  const float nn = __builtin_rintf(-a * kLog2e);                 // -n
+  const float t = __builtin_fmaf(nn, kLn2Lo, __builtin_fmaf(nn, kLn2Hi, a));
+  // v_exp_f32 on -t log2 e in [-0.5, 0.5] (no range handling needed), then 2^-n
+  const float e = __builtin_ldexpf(__builtin_amdgcn_exp2f(-t * kLog2e), (int)nn);
   const float r = __builtin_amdgcn_rcpf(1.0f + e);
   const float er = e * r;
   return g >= 0.0f ? SigPair{r, er} : SigPair{er, r};

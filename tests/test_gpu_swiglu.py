@@ -52,10 +52,13 @@ def assert_within_one_ulp(got, want, what, max_off_fraction=MAX_OFF_FRACTION):
     return off
 
 
-# Gates spread over [-120, 120]: the FP32 relative error grows like
-# (|g| + 5) 2^-24 (the rounding of |g| log2(e) before v_exp), about 65 2^-24
-# on average, and an element rounds to the other BF16 neighbour with
-# probability about twice that over the BF16 spacing 2^-8: ~0.2% expected.
+# Gates spread over [-120, 120].  The exponential's argument is range-reduced,
+# so its error no longer grows with |g|; what remains off by one BF16 ulp:
+# for 17 < g < 40 the FP32 sigmoid rounds to exactly 1, so H = g * u, a
+# product of two BF16 values, can sit exactly on a BF16 tie that the exact
+# value lies just below (about one element in 256 of that band); for
+# |g| > 87 exp(-|g|) is an FP32 denormal with fewer significant bits.
+# Measured 53 of 32768 (H) and 21 of 32768 (dY_gu); the bound keeps margin.
 EXTREME_OFF_FRACTION = 5e-3
 
 
