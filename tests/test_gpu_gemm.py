@@ -65,6 +65,26 @@ def test_nvfp4_shape_sweep(M, N, K):
     _check(C, G.gemm_nvfp4(oac, oas, oaa, obc, obs, oba), f"nvfp4 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 520, 768), (512, 272, 1280), (560, 768, 1792)])
+def test_nvfp4_odd_pair_counts(M, N, K):
+    """K = 768, 1280, 1792: 3, 5 and 7 pairs of 128-element K units, so the
+    register-expansion kernel's last pair lands in the other of its two pair
+    buffers than with the even pair counts of the other shapes; several
+    waves of ragged tiles; run twice, bit-identical."""
+    announce("nvfp4 odd pairs", M, N, K)
+    A = synth.bf16_tensor((M, K), 3000 + M + K, device="cuda")
+    B = synth.bf16_tensor((N, K), 4000 + N + K, sigma=0.02, outliers=False, device="cuda")
+    ac, as_, aa = bsq.nvfp4_quantize(A, 1)
+    bc, bs, ba = bsq.nvfp4_quantize(B, 1)
+    C = bsq.bs_gemm("nvfp4", ac, as_, bc, bs, aa, ba)
+    C2 = bsq.bs_gemm("nvfp4", ac, as_, bc, bs, aa, ba)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+    oac, oas, oaa = Q.nvfp4_quantize(bits(A), 1)
+    obc, obs, oba = Q.nvfp4_quantize(bits(B), 1)
+    _check(C, G.gemm_nvfp4(oac, oas, oaa, obc, obs, oba), f"nvfp4 {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("M,N,K", [(16, 16, 32), (48, 272, 96), (256, 256, 256), (512, 768, 384),
                                    (300, 48, 4096),
