@@ -523,7 +523,9 @@ def route_ceilings(device, iters=4000, blocks=1024):
     plus the VALU rescale acc += sA * sB * P, on the FP16 32x32x16 MFMA and on
     the scaled FP4 32x32x64 MFMA (one 16-block per instruction); route (b)'s
     FP16 MFMAs accumulating directly; and the scaled FP4 MFMA accumulating
-    directly over all 64 K positions (the MXFP4 instruction's own ceiling).
+    directly over all 64 K positions (the MXFP4 instruction's own ceiling);
+    route (b) on the 16x16x32 FP16 MFMA the GEMM uses, alone and with one
+    expansion pair (two VALU operations) per MFMA as in the GEMM's loop.
     Useful flops only (a 16-block per route-(a) instruction).  Two timed
     launches each (HIP events on the launch stream), the second reported."""
     path = os.path.join(ROOT, "fp8_quantized_gemm_amd", "libbsq_ceiling.so")
@@ -537,7 +539,9 @@ def route_ceilings(device, iters=4000, blocks=1024):
     for mode, key, kmul, peak in ((1, "route_b_fp16_mfma_only", 1, PEAK_FP16_TFLOPS),
                                   (0, "route_a_fp16_mfma_plus_valu_rescale", 1, PEAK_FP16_TFLOPS),
                                   (2, "route_a_scaled_fp4_mfma_plus_valu_rescale", 1, PEAK_FP16_TFLOPS),
-                                  (3, "mxfp4_scaled_mfma_only", 4, PEAK_FP4_TFLOPS)):
+                                  (3, "mxfp4_scaled_mfma_only", 4, PEAK_FP4_TFLOPS),
+                                  (4, "route_b_fp16_16x16x32_mfma_only", 0.5, PEAK_FP16_TFLOPS),
+                                  (5, "route_b_fp16_16x16x32_mfma_plus_expansion_pair", 0.5, PEAK_FP16_TFLOPS)):
         for _ in range(2):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -552,7 +556,7 @@ def route_ceilings(device, iters=4000, blocks=1024):
     out["note"] = ("MFMA loops with operands in registers; route (a) counts the 16-block's flops "
                    "(the scaled FP4 instruction runs 64 K positions, 48 of them zero); the "
                    "complete route (b) GEMM (roofline.achieved) includes all memory traffic and "
-                   "the expansion")
+                   "the expansion, whose instruction mix the 16x16x32 plus-expansion loop has")
     return out
 
 

@@ -225,7 +225,7 @@ def test_ceiling_library_loads_and_checks_arguments():
     L = ctypes.CDLL(path)
     L.bsq_route_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.bsq_route_ceiling.restype = ctypes.c_int
-    assert L.bsq_route_ceiling(4, FAKE, 1, 1, None) == -1        # no such mode
+    assert L.bsq_route_ceiling(6, FAKE, 1, 1, None) == -1        # no such mode
     assert L.bsq_route_ceiling(0, None, 1, 1, None) == -1        # no sink
     assert L.bsq_route_ceiling(1, FAKE, 1, 0, None) == -1        # no workgroups
     assert not hasattr(bsq.lib(), "bsq_route_ceiling")           # not part of the product ABI
