@@ -17,7 +17,14 @@ around them, which these checks read from a fresh `hipcc -S` of the source:
 
 Wait states are counted as issued instructions between the two, an s_nop N
 counting N + 1.  The checker itself is pinned on small synthetic listings.
-No GPU is needed; the test is skipped without hipcc."""
+No GPU is needed; the test is skipped without hipcc.
+
+The quantizer's stochastic FP4 packs are inline assembly too, for the same
+reason (the byte of the destination word they write is kept fixed, the other
+bytes tied through).  gfx950 needs one wait state between such a
+byte-selected result and the next VALU instruction that reads the register
+(the compiler inserts exactly one after its own builtin); the fifth rule
+checks that every function of the quantizer source keeps it."""
 
 import os
 import re
@@ -106,6 +113,46 @@ def hazards(lines, acc_read_ws=18, acc_write_ws=4, frag_ws=2):
     return bad
 
 
+_SR_PACK = re.compile(r"^v_cvt_scalef32_sr_pk_fp4_f32\s+(v\d+),.*op_sel:\[(\d),(\d),(\d),(\d)\]")
+
+
+def _source_regs(tok):
+    """Register operand of a source token, modifiers (neg, abs, sdwa and
+    op_sel suffixes) stripped."""
+    tok = tok.strip().split()[0] if tok.strip() else tok
+    return _regs(tok.lstrip("-|").rstrip("|"))
+
+
+def sr_pack_hazards(lines, ws_needed=1):
+    """Violations (index, text) of the fifth rule: a VALU instruction reads
+    the destination of a byte-selected stochastic FP4 pack (op_sel naming
+    byte 1, 2 or 3) fewer than ws_needed wait states after it."""
+    text = []
+    for line in lines:
+        t = line.split(";")[0].strip()
+        if t and not t.startswith(".") and not t.endswith(":"):
+            text.append(t)
+    ins = _instructions(lines)
+    bad = []
+    for i, t in enumerate(text):
+        m = _SR_PACK.match(t)
+        if not m or (m.group(4) == "0" and m.group(5) == "0"):
+            continue
+        dst = _regs(m.group(1))
+        ws = 0
+        for j in range(i + 1, len(ins)):
+            mn, ops = ins[j]
+            if ws >= ws_needed:
+                break
+            if mn.startswith("v_"):
+                # a later byte-selected pack also reads its own destination
+                srcs = ops if _SR_PACK.match(text[j]) else ops[1:]
+                if any(_overlap(_source_regs(o), dst) for o in srcs):
+                    bad.append((j, f"{mn} reads {m.group(1)} {ws} wait states after a byte-selected SR pack"))
+            ws += _weight(ins[j])
+    return bad
+
+
 def _functions(asm, name_part):
     """{symbol: body lines} of the functions whose symbol contains name_part."""
     funcs, cur = {}, None
@@ -154,6 +201,24 @@ def test_checker_flags_fragment_written_just_before_mfma():
     assert hazards(spaced) == []
     # a write of a register the MFMA does not read is no hazard
     assert hazards(["\tv_pk_mul_f16 v30, v20, v21", lines[1]]) == []
+
+
+def test_checker_flags_sr_pack_read_without_wait_state():
+    pack = "\tv_cvt_scalef32_sr_pk_fp4_f32 v5, v[0:1], v2, 1.0 op_sel:[0,0,1,0]"
+    read = "\tv_and_b32_e32 v6, 0xf0f0f0f, v5"
+    assert len(sr_pack_hazards([pack, read])) == 1
+    assert sr_pack_hazards([pack, "\ts_nop 0", read]) == []
+    # another instruction in between is the wait state
+    assert sr_pack_hazards([pack, "\tv_lshlrev_b32_e32 v9, 16, v8", read]) == []
+    # the next pack into the same word reads it (tied bytes)
+    tied = "\tv_cvt_scalef32_sr_pk_fp4_f32 v5, v[10:11], v3, 1.0 op_sel:[0,0,0,1]"
+    assert len(sr_pack_hazards([pack, tied])) == 1
+    # byte 0 needs no wait state, and a write of another register is no hazard
+    byte0 = "\tv_cvt_scalef32_sr_pk_fp4_f32 v5, v[0:1], v2, 1.0"
+    assert sr_pack_hazards([byte0, read]) == []
+    assert sr_pack_hazards([pack, "\tv_and_b32_e32 v6, 0xf0f0f0f, v7"]) == []
+    # source modifiers and sdwa suffixes do not hide a read
+    assert len(sr_pack_hazards([pack, "\tv_lshlrev_b32_sdwa v1, v2, v5 dst_sel:DWORD src1_sel:BYTE_1"])) == 1
 
 
 # ------------------------------------------------------------------ the kernel
@@ -209,3 +274,18 @@ def test_mx_mfma_operand_timing(mx_asm):
     funcs = _functions(mx_asm, "k_gemm_mx_rx")
     assert len(funcs) == 3, list(funcs)                       # MXFP4, MXFP8, per-tensor FP8
     _check_kernels(funcs)
+
+
+@pytest.fixture(scope="module")
+def quant_asm():
+    return _compile("bsq_quantize.hip")
+
+
+def test_sr_pack_wait_states(quant_asm):
+    funcs = _functions(quant_asm, "bsq")
+    packs, report = 0, []
+    for name, body in funcs.items():
+        packs += sum(1 for line in body if "v_cvt_scalef32_sr_pk_fp4_f32" in line and "op_sel" in line)
+        report += [f"{name}: {t}" for _, t in sr_pack_hazards(body)]
+    assert packs > 0, "no byte-selected SR pack found"
+    assert report == [], "\n".join(report[:20])
